@@ -1,0 +1,174 @@
+/*
+ * tssample.h -- C ABI of the MI355X (gfx950) batched token sampler.
+ *
+ * One call samples one token id per output row from a logits matrix
+ * [rows_in_buffer, vocab] and (optionally) returns the log-prob of that id
+ * under the processed distribution.  The operation is the one described by
+ *   - "core.inference.sampling.base" (Megatron-Core API docs), class Sampling,
+ *     methods sample_kernel (gather_indices, token_to_request_index, n rows of
+ *     a [>=n, vocab] logits tensor, returns ids [n]) and sample_speculative
+ *     (decode requests contribute 1 + num_speculative_tokens rows, prefill
+ *     requests 1 row);
+ *   - "core.inference.sampling.flashinfer_sampling" (Megatron-Core API docs),
+ *     class FlashInferSampling: per-step top-p-only / top-k-only / joint
+ *     dispatch from CPU-side flags no_top_k / no_top_p (no GPU sync), seeded
+ *     Philox randomness that advances per step, caller-owned output [n], and
+ *     log_probs_kernel (log-probs of the processed distribution);
+ *   - the TokenSpeed Triton sampling backend source page: per-request pools of
+ *     temperature / top_k / top_p / 64-bit seed, Gumbel-max sampling, int32
+ *     index arrays.
+ *
+ * Per output row r (0 <= r < n):
+ *   src = gather_indices ? gather_indices[r] : r      row of the logits buffer
+ *   q   = token_to_request_index ? token_to_request_index[r] : r   parameter slot
+ *   x   = logits[src, 0:vocab] (NaN read as -inf, -0 as +0)
+ *   K   = top-k set: the first min(k, #finite) indices in the order
+ *         (x descending, index ascending) when 1 <= k < vocab, else all finite
+ *   s   = x / temperature[q]  (temperature < 1e-5 means greedy: first index of
+ *         that order, log-prob 0)
+ *   P   = top-p set inside K: j is kept when the softmax(s)-mass over K of the
+ *         members with a strictly larger logit is below p; p >= 1 - 1e-6 keeps
+ *         all of K; the top tie group is always kept
+ *   g_j = -ln(-ln u_j), u_j = ((w_j >> 9) + 1/2) * 2^-23, w_j = word (j & 3) of
+ *         Philox4x32-10(key = seed[q], counter = (j >> 2, r, step_offset lo,
+ *         step_offset hi))  (Salmon et al., SC'11)
+ *   id  = argmax over P of s_j + g_j (smallest j on exact ties)
+ *   lp  = s_id - logsumexp over P of s
+ * A row whose entries are all -inf/NaN yields id -1 and lp NaN.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers named "device" are device memory of the sampler's GPU; the
+ *     caller owns every buffer.  The library never allocates inside ts_sample /
+ *     ts_log_probs.
+ *   - "stream" is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *     work and return without synchronising; results are valid once the stream
+ *     has reached them.  A sampler handle may be used from one host thread at
+ *     a time.
+ *   - Errors are returned as ts_status, never thrown.  Host-checkable argument
+ *     errors are detected before any work is enqueued.  Out-of-range values
+ *     inside device arrays (gather / map / token ids) are the caller's
+ *     responsibility and are not checked.
+ */
+#ifndef TSSAMPLE_H
+#define TSSAMPLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ts_status {
+  TS_OK = 0,
+  TS_E_ARG = 1,    /* null pointer, negative size or inconsistent argument */
+  TS_E_DTYPE = 2,  /* unsupported logits dtype */
+  TS_E_SIZE = 3,   /* n above max_rows, stride below vocab, rows_in_buffer below n, ... */
+  TS_E_HIP = 4,    /* a HIP runtime call failed (launch, device query, ...) */
+  TS_E_NOMEM = 5   /* device memory for the handle's workspace could not be allocated */
+} ts_status;
+
+typedef enum ts_dtype {
+  TS_F32 = 0,      /* IEEE binary32 logits */
+  TS_BF16 = 1      /* bfloat16 logits (upper half of a binary32) */
+} ts_dtype;
+
+/* Filter routes chosen on the host from the batch-level flags (no GPU sync):
+ * "flashinfer_sampling": dedicated top-p or top-k kernel when only one filter is
+ * in use, joint kernel only for mixed batches. */
+typedef enum ts_route {
+  TS_ROUTE_NONE = 0,   /* no_top_k && no_top_p */
+  TS_ROUTE_TOPK = 1,   /* !no_top_k && no_top_p */
+  TS_ROUTE_TOPP = 2,   /* no_top_k && !no_top_p */
+  TS_ROUTE_JOINT = 3   /* !no_top_k && !no_top_p */
+} ts_route;
+
+typedef struct ts_sampler ts_sampler;
+
+/* Per-request sampling parameters, structure of arrays, device memory, indexed
+ * by the request slot q.  top_k may be NULL when the call passes no_top_k = 1 and
+ * top_p may be NULL when it passes no_top_p = 1: the flags are promises that no
+ * row uses that filter, and the route then never reads the array. */
+typedef struct ts_params {
+  const float* temperature;   /* [num_requests] */
+  const int32_t* top_k;       /* [num_requests]; k <= 0 or k >= vocab: filter off */
+  const float* top_p;         /* [num_requests]; p >= 1 - 1e-6: filter off */
+  const uint64_t* seed;       /* [num_requests] */
+  int32_t num_requests;       /* > 0 */
+} ts_params;
+
+/* Create a sampler for logits rows of `vocab` entries and up to `max_rows`
+ * output rows per call on HIP device `device`.  Any device memory the handle
+ * needs is allocated here, once; ts_sample / ts_log_probs allocate nothing.
+ * device == -1 creates a validation-only handle: its calls run every host-side
+ * argument check and then return TS_E_HIP without touching a GPU (useful to
+ * test callers on a machine without one).
+ * Errors: TS_E_ARG (out == NULL, vocab < 1, vocab >= 2^31, max_rows < 1,
+ * device < -1), TS_E_HIP (no such device), TS_E_NOMEM. */
+ts_status ts_create(int64_t vocab, int32_t max_rows, int32_t device, ts_sampler** out);
+
+/* Release a sampler (NULL is accepted).  The caller must ensure no enqueued
+ * call on it is still running. */
+ts_status ts_destroy(ts_sampler* sampler);
+
+/* Sample one id per output row (see the top of this file for the definition).
+ *   logits          device, row-major [rows_in_buffer, row_stride] of `dtype`;
+ *                   only the first `vocab` entries of a row are read
+ *   rows_in_buffer  rows present in `logits` (>= n when gather_indices is NULL)
+ *   row_stride      elements between consecutive rows (>= vocab)
+ *   n               output rows, 0 <= n <= max_rows (n == 0 enqueues nothing)
+ *   gather_indices  device int32 [n] or NULL
+ *   token_to_request_index  device int32 [n] or NULL (NULL: q = r, which then
+ *                   needs params->num_requests >= n)
+ *   params          host struct of device arrays
+ *   step_offset     Philox offset of this call (advance it between steps)
+ *   no_top_k, no_top_p  batch-level flags (0/1) computed by the caller on the host
+ *   out_ids         device int32 [n], written
+ *   out_logprob     device float [n] or NULL, written when non-NULL
+ *   stream          hipStream_t
+ * Errors: TS_E_ARG, TS_E_DTYPE, TS_E_SIZE (host-side checks), TS_E_HIP (launch). */
+ts_status ts_sample(ts_sampler* sampler, const void* logits, ts_dtype dtype,
+                    int64_t rows_in_buffer, int64_t row_stride, int32_t n,
+                    const int32_t* gather_indices, const int32_t* token_to_request_index,
+                    const ts_params* params, uint64_t step_offset,
+                    int32_t no_top_k, int32_t no_top_p,
+                    int32_t* out_ids, float* out_logprob, void* stream);
+
+/* Log-probs of the processed distribution ("flashinfer_sampling",
+ * log_probs_kernel): for every output row, lp_j = s_j - logsumexp_P(s) for j in
+ * P and -inf outside P (greedy rows: 0 at the greedy id, -inf elsewhere; rows
+ * with no finite logit: NaN).  Arguments as for ts_sample, plus
+ *   token_ids  device int32 [n] or NULL
+ *   out        device float: [n, vocab] row-major when token_ids is NULL, else [n]
+ *              holding lp at token_ids[r]
+ * Errors: as ts_sample. */
+ts_status ts_log_probs(ts_sampler* sampler, const void* logits, ts_dtype dtype,
+                       int64_t rows_in_buffer, int64_t row_stride, int32_t n,
+                       const int32_t* gather_indices, const int32_t* token_to_request_index,
+                       const ts_params* params, int32_t no_top_k, int32_t no_top_p,
+                       const int32_t* token_ids, float* out, void* stream);
+
+/* Per-row request index of the speculative-verify layout
+ * ("core.inference.sampling.base", sample_speculative): decode request d in
+ * [0, num_decode) owns rows d*(1+num_spec) .. d*(1+num_spec)+num_spec, prefill
+ * request i owns row num_decode*(1+num_spec)+i and has index num_decode+i.
+ * Writes n = num_decode*(1+num_spec)+num_prefill entries of out_map (capacity
+ * entries available); with on_device != 0 out_map is device memory and the
+ * write is enqueued on `stream`, else it is host memory written synchronously.
+ * *out_n (host) receives n.
+ * Errors: TS_E_ARG (negative counts, NULL pointers), TS_E_SIZE (capacity < n),
+ * TS_E_HIP. */
+ts_status ts_build_spec_map(int32_t num_decode, int32_t num_prefill, int32_t num_spec,
+                            int32_t* out_map, int32_t capacity, int32_t on_device,
+                            void* stream, int32_t* out_n);
+
+/* The route the flags select (pure host function, no GPU). */
+ts_route ts_select_route(int32_t no_top_k, int32_t no_top_p);
+
+/* Static text for a status code. */
+const char* ts_status_str(ts_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSSAMPLE_H */

@@ -1,0 +1,112 @@
+"""Host-side tests of the C ABI: the library loads, exports what the header
+declares, routes flags, and rejects bad arguments before touching a GPU."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import token_sampling_scaled_amd as tsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tssample.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tsa.LIB_PATH):
+        from token_sampling_scaled_amd import build
+        build.build()
+    return tsa.library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ts_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert "ts_sample" in names and "ts_log_probs" in names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_routes(lib):
+    for code in range(6):
+        assert lib.ts_status_str(code)
+    # "flashinfer_sampling": dedicated kernels for one filter, joint for mixed batches
+    assert lib.ts_select_route(1, 1) == tsa.ROUTE_NONE
+    assert lib.ts_select_route(0, 1) == tsa.ROUTE_TOPK
+    assert lib.ts_select_route(1, 0) == tsa.ROUTE_TOPP
+    assert lib.ts_select_route(0, 0) == tsa.ROUTE_JOINT
+
+
+def test_create_argument_errors(lib):
+    h = ctypes.c_void_p()
+    assert lib.ts_create(0, 4, -1, ctypes.byref(h)) == tsa.TS_E_ARG
+    assert lib.ts_create(100, 0, -1, ctypes.byref(h)) == tsa.TS_E_ARG
+    assert lib.ts_create(2**31, 4, -1, ctypes.byref(h)) == tsa.TS_E_ARG
+    assert lib.ts_create(100, 4, -2, ctypes.byref(h)) == tsa.TS_E_ARG
+    assert lib.ts_create(100, 4, -1, None) == tsa.TS_E_ARG
+
+
+FAKE = 0x10000   # never dereferenced: a validation-only handle enqueues nothing
+
+
+def _params(temperature=FAKE, top_k=FAKE, top_p=FAKE, seed=FAKE, q=8):
+    return tsa._Params(temperature, top_k, top_p, seed, q)
+
+
+def test_sample_argument_checks_on_validation_handle(lib):
+    h = ctypes.c_void_p()
+    assert lib.ts_create(100, 8, -1, ctypes.byref(h)) == tsa.TS_OK
+    try:
+        def call(logits=FAKE, dtype=tsa.TS_BF16, rows=8, stride=100, n=8, gather=None, req=None,
+                 params=None, nk=0, np_=0, out=FAKE, lp=None):
+            p = params if params is not None else _params()
+            return lib.ts_sample(h, logits, dtype, rows, stride, n, gather, req, ctypes.byref(p),
+                                 0, nk, np_, out, lp, None)
+        assert call() == tsa.TS_E_HIP                      # all checks pass, no GPU on this handle
+        assert call(n=0) == tsa.TS_OK                      # nothing to do
+        assert call(dtype=7) == tsa.TS_E_DTYPE
+        assert call(n=9) == tsa.TS_E_SIZE                  # above max_rows
+        assert call(n=-1) == tsa.TS_E_ARG
+        assert call(stride=99) == tsa.TS_E_SIZE            # stride below vocab
+        assert call(rows=4) == tsa.TS_E_SIZE               # fewer rows than n, no gather
+        assert call(rows=4, gather=FAKE) == tsa.TS_E_HIP   # gathered rows may repeat
+        assert call(logits=None) == tsa.TS_E_ARG
+        assert call(out=None) == tsa.TS_E_ARG
+        assert call(params=_params(top_k=None)) == tsa.TS_E_ARG           # k used, array missing
+        assert call(params=_params(top_k=None), nk=1) == tsa.TS_E_HIP     # flag promises no top-k
+        assert call(params=_params(top_p=None)) == tsa.TS_E_ARG
+        assert call(params=_params(top_p=None), np_=1) == tsa.TS_E_HIP
+        assert call(params=_params(temperature=None)) == tsa.TS_E_ARG
+        assert call(params=_params(seed=None)) == tsa.TS_E_ARG
+        assert call(params=_params(q=4)) == tsa.TS_E_SIZE                 # q = r needs >= n slots
+        assert call(params=_params(q=4), req=FAKE) == tsa.TS_E_HIP
+        assert call(params=_params(q=0), req=FAKE) == tsa.TS_E_ARG
+        p = _params()
+        assert lib.ts_log_probs(h, FAKE, tsa.TS_F32, 8, 100, 8, None, None, ctypes.byref(p),
+                                0, 0, None, None, None) == tsa.TS_E_ARG   # no output
+        assert lib.ts_log_probs(h, FAKE, tsa.TS_F32, 8, 100, 8, None, None, ctypes.byref(p),
+                                0, 0, None, FAKE, None) == tsa.TS_E_HIP
+        assert lib.ts_sample(None, FAKE, 0, 8, 100, 8, None, None, ctypes.byref(p), 0, 0, 0,
+                             FAKE, None, None) == tsa.TS_E_ARG
+    finally:
+        lib.ts_destroy(h)
+
+
+def test_spec_map_on_host(lib):
+    with open(os.path.join(ROOT, "tests", "golden", "spec_layout.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        m, n = tsa.build_spec_map(c["num_decode"], c["num_prefill"], c["num_spec"])
+        assert n == len(c["map"]) and m.tolist() == c["map"]
+    got = ctypes.c_int32()
+    buf = (ctypes.c_int32 * 4)()
+    assert lib.ts_build_spec_map(2, 2, 3, buf, 4, 0, None, ctypes.byref(got)) == tsa.TS_E_SIZE
+    assert got.value == 10
+    assert lib.ts_build_spec_map(-1, 2, 3, buf, 4, 0, None, ctypes.byref(got)) == tsa.TS_E_ARG

@@ -1,0 +1,179 @@
+"""GPU parity: the HIP sampler against the fp64 oracle on the same seeded inputs.
+
+Bars: top-k sets bit-exact; top-p sets and sampled ids exact except rows the
+oracle flags as near ties within 1e-5 relative (counted, and the GPU must take
+one of the listed alternatives); log-probs within 1e-4 absolute.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import token_sampling_scaled_amd as tsa
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    ("tiny_joint", None, None),
+    ("none_32k", 16, 32000),
+    ("topk_128k", 12, 20011),      # odd vocab: rows not vector aligned, ragged tail
+    ("joint_128k", 12, 20000),
+    ("topp_152k", 8, 30000),
+    ("spec_mix", 24, 16384),
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tsa.library()
+
+
+@pytest.mark.parametrize("name,rows,vocab", SMALL)
+def test_sample_parity_small(name, rows, vocab):
+    wl = synth.make(name, rows=rows, vocab=vocab)
+    print(f"[case] sample {name} rows={wl.n} vocab={wl.vocab} dtype={wl.logits.dtype}", flush=True)
+    ids, lps = parity.gpu_sample(wl)
+    parity.compare_samples(ids, lps, parity.oracle_sample(wl)).check()
+
+
+@pytest.mark.parametrize("name,rows,vocab", SMALL)
+def test_log_probs_parity_small(name, rows, vocab):
+    wl = synth.make(name, rows=rows, vocab=vocab)
+    print(f"[case] log_probs {name} rows={wl.n} vocab={wl.vocab}", flush=True)
+    gpu = parity.gpu_log_probs(wl)
+    ref = parity.oracle_log_probs(wl)
+    res = parity.oracle_sample(wl)
+    parity.compare_log_probs(gpu, ref, res).check()
+    # log-probs at the sampled ids equal the fused log-prob of sample()
+    ids, lps = parity.gpu_sample(wl)
+    at = parity.gpu_log_probs(wl, token_ids=torch.from_numpy(ids.astype(np.int32)))
+    fin = ids >= 0
+    assert np.allclose(at[fin], lps[fin], atol=1e-5, rtol=0)
+
+
+@pytest.mark.parametrize("name", ["tiny_joint", "none_32k", "topk_128k", "joint_128k",
+                                  "topp_152k", "spec_mix"])
+def test_sample_parity_full_size_sampled_rows(name):
+    wl = synth.make(name)
+    print(f"[case] full {name} rows={wl.n} vocab={wl.vocab}", flush=True)
+    ids, lps = parity.gpu_sample(wl)
+    rows = sorted(set(np.linspace(0, wl.n - 1, 10).astype(int).tolist()))
+    rep = parity.compare_samples(ids, lps, parity.oracle_sample(wl, rows=rows), rows=rows)
+    rep.check()
+    assert np.all((ids >= 0) & (ids < wl.vocab))
+
+
+def _custom(rows, dtype=torch.float32, k=0, p=1.0, t=1.0, no_top_k=None, no_top_p=None,
+            stride_pad=0):
+    x = torch.tensor(np.array(rows, dtype=np.float32)).to(dtype)
+    n, v = x.shape
+    wl = synth.Workload("custom", x, n, torch.full((n,), float(t)), torch.full((n,), int(k), dtype=torch.int32),
+                        torch.full((n,), float(p)), torch.arange(n, dtype=torch.int64) + 11)
+    wl.no_top_k = (k == 0) if no_top_k is None else no_top_k
+    wl.no_top_p = (p >= 1.0) if no_top_p is None else no_top_p
+    wl.stride_pad = stride_pad
+    return wl
+
+
+def _device_logits(wl):
+    pad = getattr(wl, "stride_pad", 0)
+    if not pad:
+        return wl.logits.cuda()
+    buf = torch.full((wl.n, wl.vocab + pad), 7.0, dtype=wl.logits.dtype, device="cuda")
+    buf[:, :wl.vocab] = wl.logits.cuda()
+    return buf[:, :wl.vocab]
+
+
+def _run_custom(wl):
+    dev = {"logits": _device_logits(wl), "gather": None, "req": None,
+           "params": tsa.SamplingParams(wl.temperature.cuda(), wl.seed.cuda(), wl.top_k.cuda(),
+                                        wl.top_p.cuda())}
+    s = tsa.Sampler(wl.vocab, wl.n)
+    ids, lps = parity.gpu_sample(wl, s, dev)
+    parity.compare_samples(ids, lps, parity.oracle_sample(wl)).check()
+    gpu = parity.gpu_log_probs(wl, s, dev)
+    parity.compare_log_probs(gpu, parity.oracle_log_probs(wl), parity.oracle_sample(wl)).check()
+    return ids, lps
+
+
+EDGE_ROWS = {
+    "ties": [[1.0, 3.0, 3.0, 2.0, 3.0, -0.0, 0.0, 3.0]] * 3,
+    "neg_inf_nan": [[-np.inf, 1.0, np.nan, 2.0, -np.inf, 0.5, np.nan, -1.0]],
+    "all_neg_inf": [[-np.inf] * 5, [np.nan] * 5],
+    "single": [[0.25]],
+    "three": [[0.1, 0.1, 0.1]],
+}
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("case", sorted(EDGE_ROWS))
+@pytest.mark.parametrize("k,p,t", [(0, 1.0, 1.0), (2, 1.0, 0.8), (0, 0.5, 1.3), (3, 0.7, 1.0),
+                                   (1, 1.0, 1.0), (0, 0.0, 1.0), (0, 1.0, 0.0), (100, 0.9, 1.0)])
+def test_edge_rows(case, dtype, k, p, t):
+    wl = _custom(EDGE_ROWS[case], dtype=dtype, k=k, p=p, t=t)
+    print(f"[case] edge {case} {dtype} k={k} p={p} t={t}", flush=True)
+    _run_custom(wl)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_bf16_like_ties_and_misaligned_stride(dtype):
+    rng = np.random.default_rng(12)
+    rows = np.round(rng.normal(0, 3, size=(6, 3001)) * 4) / 4     # heavy ties
+    for k, p in [(50, 1.0), (700, 0.8), (0, 0.6), (1, 0.9)]:
+        wl = _custom(rows, dtype=dtype, k=k, p=p, t=0.9, stride_pad=3)
+        print(f"[case] ties k={k} p={p} {dtype}", flush=True)
+        _run_custom(wl)
+
+
+def test_determinism_and_step_offset():
+    wl = synth.make("spec_mix", rows=24, vocab=16384)
+    dev = parity.to_device(wl)
+    s = tsa.Sampler(wl.vocab, wl.n)
+    a = parity.gpu_sample(wl, s, dev)
+    b = parity.gpu_sample(wl, s, dev)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    c = parity.gpu_sample(wl, s, dev, step_offset=1)
+    assert not np.array_equal(a[0], c[0])
+    parity.compare_samples(*c, parity.oracle_sample(wl, step_offset=1)).check()
+
+
+def test_gather_identity_and_int64_indices():
+    wl = synth.make("spec_mix", rows=24, vocab=4096)
+    dev = parity.to_device(wl)
+    s = tsa.Sampler(wl.vocab, wl.n)
+    ids, lps = s.sample(dev["logits"], wl.n, dev["params"], gather_indices=dev["gather"].long(),
+                        token_to_request_index=dev["req"].long(), return_logprobs=True)
+    pre = dev["logits"][dev["gather"].long()].contiguous()
+    ids2, lps2 = s.sample(pre, wl.n, dev["params"], token_to_request_index=dev["req"],
+                          return_logprobs=True)
+    assert torch.equal(ids, ids2) and torch.equal(lps, lps2)
+    with pytest.raises(ValueError):
+        s.sample(dev["logits"], wl.n, dev["params"], gather_indices=dev["gather"].float())
+
+
+def test_sample_speculative_matches_explicit_map():
+    wl = synth.make("spec_mix")
+    dev = parity.to_device(wl)
+    s = tsa.Sampler(wl.vocab, wl.n)
+    a = s.sample_speculative(dev["logits"], 64, 32, 3, dev["params"], gather_indices=dev["gather"])
+    b = s.sample(dev["logits"], wl.n, dev["params"], gather_indices=dev["gather"],
+                 token_to_request_index=dev["req"])
+    assert torch.equal(a, b)
+    m, n = tsa.build_spec_map(64, 32, 3, device="cuda")
+    assert n == 288 and torch.equal(m.cpu(), wl.token_to_request_index)
+
+
+def test_argument_errors_on_gpu_handle():
+    s = tsa.Sampler(100, 4)
+    x = torch.zeros(4, 100, device="cuda")
+    prm = tsa.SamplingParams(torch.ones(4, device="cuda"), torch.zeros(4, dtype=torch.int64, device="cuda"),
+                             torch.zeros(4, dtype=torch.int32, device="cuda"), torch.ones(4, device="cuda"))
+    with pytest.raises(ValueError):
+        s.sample(x, 5, prm)                       # n > max_rows
+    with pytest.raises(TypeError):
+        s.sample(x.half(), 4, prm)
+    out = s.sample(x, 0, prm)
+    assert out.numel() == 0

@@ -1,0 +1,83 @@
+"""Build libtssample.so (gfx950) in-tree with hipcc.
+
+    python -m token_sampling_scaled_amd.build          # compile every source
+
+Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
+generation switched off, and linked with the C-ABI host code into one shared
+library next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libtssample.so")
+
+ARCH = "gfx950"
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libtssample.so")
+
+
+def sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    cc = hipcc()
+    objdir = tempfile.mkdtemp(prefix="tssample_build_")
+    try:
+        procs = []
+        objs = []
+        for src in sources():
+            obj = os.path.join(objdir, os.path.basename(src) + ".o")
+            objs.append(obj)
+            cmd = [cc, *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", src, "-o", obj]
+            if src.endswith(".cpp"):
+                cmd[1:1] = ["-x", "hip"]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+            if len(procs) >= jobs:
+                _wait(procs.pop(0))
+        for p in procs:
+            _wait(p)
+        tmp = LIB + ".tmp"
+        link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        subprocess.run(link, check=True)
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
+    return LIB
+
+
+def _wait(item):
+    src, proc = item
+    out, _ = proc.communicate()
+    if proc.returncode != 0:
+        sys.stderr.write(out.decode(errors="replace"))
+        raise RuntimeError(f"hipcc failed on {os.path.basename(src)}")
+    if out.strip():
+        sys.stderr.write(out.decode(errors="replace"))
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

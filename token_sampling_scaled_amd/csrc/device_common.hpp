@@ -1,0 +1,149 @@
+// Device helpers shared by the sampling kernels (gfx950, wave64).
+//
+// Order keys, the Philox4x32-10 counter-based generator, the integer -> Gumbel
+// transform and wave / block reductions.  Nothing here is shared with the CPU
+// oracle: both follow the same published definitions independently.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tss {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Order keys: unsigned integers whose order is the order of the logits, with
+// NaN read as -inf and -0 as +0 (so equal logits have equal keys).  Keys of
+// finite values and +inf are strictly above key(-inf).
+
+struct KeyF32 {
+  static constexpr int kBits = 32;
+  static constexpr uint32_t kNegInf = 0x007FFFFFu;          // key of 0xFF800000
+  __device__ __forceinline__ static uint32_t from_bits(uint32_t u) {
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) u = 0xFF800000u;     // NaN -> -inf
+    if (u == 0x80000000u) u = 0u;                             // -0 -> +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+};
+
+struct KeyBF16 {
+  static constexpr int kBits = 16;
+  static constexpr uint32_t kNegInf = 0x007Fu;              // key of 0xFF80
+  __device__ __forceinline__ static uint32_t from_bits(uint32_t b) {
+    if ((b & 0x7FFFu) > 0x7F80u) b = 0xFF80u;                 // NaN -> -inf
+    if (b == 0x8000u) b = 0u;                                 // -0 -> +0
+    return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
+// as 1, 2, 3", SC'11, section 3): each round multiplies counter words 0 and 2
+// by fixed 32-bit constants, swaps and xors the halves with the key, and the
+// key advances by the Weyl constants between rounds.
+
+struct Philox4 {
+  uint32_t v[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    if (i) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+  Philox4 r;
+  r.v[0] = c0;
+  r.v[1] = c1;
+  r.v[2] = c2;
+  r.v[3] = c3;
+  return r;
+}
+
+// Noise stream of one output row: key = 64-bit seed, counter = (j >> 2, row,
+// offset lo, offset hi); vocabulary index j reads word (j & 3).
+struct NoiseStream {
+  uint32_t k0, k1, row, off_lo, off_hi;
+  __device__ __forceinline__ Philox4 block(uint32_t j4) const {
+    return philox4x32_10(j4, row, off_lo, off_hi, k0, k1);
+  }
+  __device__ __forceinline__ uint32_t word(uint32_t j) const {
+    const Philox4 b = block(j >> 2);
+    const uint32_t s = j & 3u;
+    return s == 0 ? b.v[0] : s == 1 ? b.v[1] : s == 2 ? b.v[2] : b.v[3];
+  }
+};
+
+// u = (floor(w / 2^9) + 1/2) * 2^-23 is exact in fp32, as is 1 - u.  E = -ln u,
+// evaluated as -log1p(-(1 - u)) above 1/2 so that E keeps full relative
+// precision next to u = 1; g = -ln E.
+__device__ __forceinline__ float gumbel_from_word(uint32_t w) {
+  const float u = ((float)(w >> 9) + 0.5f) * 0x1p-23f;
+  const float e = (u > 0.5f) ? -log1pf(-(1.0f - u)) : -__logf(u);
+  return -__logf(e);
+}
+
+// ---------------------------------------------------------------------------
+// Wave / block reductions (blockDim.x a multiple of 64).
+
+template <typename V>
+__device__ __forceinline__ V wave_sum(V v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = __shfl_xor(v, off, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = __shfl_xor(v, off, kWave);
+    v = o < v ? o : v;
+  }
+  return v;
+}
+
+// (score, index) pair: larger score wins, smaller index on equal scores.
+struct ArgBest {
+  float z;
+  int32_t j;
+};
+
+__device__ __forceinline__ bool better(float za, int32_t ja, float zb, int32_t jb) {
+  return za > zb || (za == zb && ja < jb);
+}
+
+__device__ __forceinline__ ArgBest wave_argbest(ArgBest a) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float oz = __shfl_xor(a.z, off, kWave);
+    const int32_t oj = __shfl_xor(a.j, off, kWave);
+    if (better(oz, oj, a.z, a.j)) {
+      a.z = oz;
+      a.j = oj;
+    }
+  }
+  return a;
+}
+
+}  // namespace tss

@@ -1,0 +1,40 @@
+// Host-side interface between the C ABI (tssample.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tss {
+
+enum Route : int { kRouteNone = 0, kRouteTopK = 1, kRouteTopP = 2, kRouteJoint = 3 };
+enum OutMode : int { kOutSample = 0, kOutLogProbFull = 1, kOutLogProbAt = 2 };
+enum DType : int { kF32 = 0, kBF16 = 1 };
+
+// Everything a row kernel needs; all pointers are device pointers.
+struct RowArgs {
+  const void* logits;
+  int64_t row_stride;          // elements between rows
+  int64_t vocab;
+  int32_t n;                   // output rows
+  const int32_t* gather;       // [n] or null
+  const int32_t* req_map;      // [n] or null
+  const float* temperature;    // [Q]
+  const int32_t* top_k;        // [Q] (null on routes without top-k)
+  const float* top_p;          // [Q] (null on routes without top-p)
+  const uint64_t* seed;        // [Q]
+  uint64_t step_offset;
+  int32_t* out_ids;            // sample: [n]
+  float* out_lp;               // sample: [n] or null; log-probs: [n, vocab] or [n]
+  const int32_t* token_ids;    // log-probs at ids: [n]
+  int32_t mass_shift;          // fixed-point scale of probability masses: 2^mass_shift
+  int32_t index_bits;          // ceil(log2(vocab)), at least 1
+};
+
+hipError_t launch_rows(const RowArgs& a, DType dtype, Route route, OutMode mode,
+                       hipStream_t stream);
+
+// Writes the speculative-verify request map (see ts_build_spec_map) to device memory.
+hipError_t launch_spec_map(int32_t num_decode, int32_t num_prefill, int32_t num_spec,
+                           int32_t* out_map, hipStream_t stream);
+
+}  // namespace tss
