@@ -1,0 +1,169 @@
+"""Throughput of one sampling step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+A step is one ts_sample call over the whole batch (every row: filters, noise,
+draw and the fused log-prob), on synthetic logits already resident in HBM.
+The default workload is 256 rows x 128256 bf16 logits with per-row top-k and
+top-p (joint route).  Inputs rotate over enough copies to exceed the 256 MB
+Infinity Cache, so each step reads its logits from HBM.
+
+Prints one JSON line: rows/s (value), logits-read GB/s, % of the 8 TB/s HBM
+peak, the roofline record of the sampling kernel (HIP events on the launch
+stream) and the CPU oracle's rate on a bounded sample of the same rows.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import synth  # noqa: E402
+import token_sampling_scaled_amd as tsa  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "sampled rows/s + logits-read GB/s, 256x128256 bf16 top-k+top-p (% HBM peak)"
+DESCRIPTIONS = {
+    "joint_128k": "256x128256 bf16 logits N(0,3^2)+spikes, per-row top-k U{1..1024} + top-p U[0.5,0.99], T U[0.5,1.5]",
+    "topk_128k": "256x128256 bf16 logits N(0,3^2)+spikes, per-row top-k U{1..1024}, T U[0.5,1.5]",
+    "none_32k": "64x32000 bf16 logits N(0,3^2), no filter",
+    "topp_152k": "256x151936 fp32 Zipf(1.1) logits, per-row top-p U[0.5,0.99]",
+    "spec_mix": "288 of 320 rows x 128256 bf16, speculative layout, mixed none/top-k/top-p/joint + log-probs",
+    "tiny_joint": "8x4096 fp32 logits, top-k 50 + top-p 0.9",
+}
+
+
+def logits_bytes(wl) -> int:
+    return wl.n * wl.vocab * wl.logits.element_size()
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The fp64 oracle, single process, on the leading rows of the same workload."""
+    import oracle
+    x = wl.logits_f64()
+    params = wl.params_numpy()
+    gather = None if wl.gather_indices is None else wl.gather_indices.numpy()
+    req = None if wl.token_to_request_index is None else wl.token_to_request_index.numpy()
+    t0 = time.perf_counter()
+    done = 0
+    while done < wl.n and time.perf_counter() - t0 < budget_s:
+        oracle.sample(x, wl.n, params, gather_indices=gather, token_to_request_index=req,
+                      step_offset=wl.step_offset, no_top_k=wl.no_top_k, no_top_p=wl.no_top_p,
+                      rows=[done])
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {wl.n} rows of the same workload, fp64 numpy, "
+                      f"one process ({dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="joint_128k", choices=sorted(synth.WORKLOAD_IDS))
+    ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: auto)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the sampler is single-GPU (rows shard with no "
+              "exchange); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if not os.path.exists(tsa.LIB_PATH):
+        from token_sampling_scaled_amd import build
+        build.build()
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    wl = synth.make(args.workload)
+    nbytes = logits_bytes(wl)
+    buf_bytes = wl.logits.numel() * wl.logits.element_size()
+    copies = args.copies or max(2, int(np.ceil(400e6 / buf_bytes)))
+    logits = [wl.logits.to(dev) for _ in range(copies)]
+    params = tsa.SamplingParams(wl.temperature.to(dev), wl.seed.to(dev), wl.top_k.to(dev),
+                                wl.top_p.to(dev))
+    gather = None if wl.gather_indices is None else wl.gather_indices.to(dev)
+    req = None if wl.token_to_request_index is None else wl.token_to_request_index.to(dev)
+    sampler = tsa.Sampler(wl.vocab, wl.n)
+    ids = torch.empty(wl.n, dtype=torch.int32, device=dev)
+    lps = torch.empty(wl.n, dtype=torch.float32, device=dev)
+
+    def step(i):
+        sampler.sample(logits[i % copies], wl.n, params, no_top_k=wl.no_top_k,
+                       no_top_p=wl.no_top_p, gather_indices=gather, token_to_request_index=req,
+                       step_offset=i, output=ids, logprob_output=lps)
+
+    if args.copy_probe_mb:
+        a = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)       # the stream ts_sample launches on
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+
+    rows_per_s = wl.n * args.steps / wall
+    gbps = nbytes * args.steps / wall / 1e9
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": rows_per_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "logits_read_gbps": gbps,
+        "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
+        "config": {"workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}",
+                   "rows": wl.n, "vocab": wl.vocab, "logits_dtype": str(wl.logits.dtype).split(".")[-1],
+                   "route": ["none", "top-k", "top-p", "joint"][tsa.select_route(wl.no_top_k, wl.no_top_p)],
+                   "input_copies": copies, "logits_bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel_ms_per_launch": kernel_ms},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -30,8 +30,14 @@ struct RowArgs {
   int32_t index_bits;          // ceil(log2(vocab)), at least 1
 };
 
+// Picks the kernel for a call (fast register-resident kernel where the row
+// shape allows it, else the general multi-pass kernel) and launches it.
 hipError_t launch_rows(const RowArgs& a, DType dtype, Route route, OutMode mode,
                        hipStream_t stream);
+
+// The general multi-pass kernel alone (every row shape).
+hipError_t launch_rows_general(const RowArgs& a, DType dtype, Route route, OutMode mode,
+                               hipStream_t stream);
 
 // Writes the speculative-verify request map (see ts_build_spec_map) to device memory.
 hipError_t launch_spec_map(int32_t num_decode, int32_t num_prefill, int32_t num_spec,

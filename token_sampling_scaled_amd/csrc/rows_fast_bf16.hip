@@ -1,0 +1,771 @@
+// Register-resident sampling kernel for bf16 rows (vocab <= 131072, vocab a
+// multiple of 8, rows 16-byte aligned): one workgroup of 1024 threads (16
+// waves) per output row; every logit is read from HBM exactly once with
+// non-temporal 16-byte loads, all issued up front, and kept in VGPRs.
+//
+// Rows with an active top-k (k <= 1024), with or without top-p.  The waves
+// work independently while the row streams in -- data reaches the 16 waves of
+// a workgroup at very different times, so no step waits for another wave until
+// the row has arrived:
+//   1. threshold: from the first half of its own data, wave w takes
+//      t_w = the c-th largest of its 16-entry group maxima (bitwise descent with
+//      ballots), c = min(k, ceil(k/16) + 4);
+//   2. filter: a 16-byte vector whose maximum reaches t_w is copied whole into
+//      the wave's LDS segment (ballot + mbcnt), and its entries >= t_w are
+//      counted in a histogram with one bin per bf16 value (a bin is exactly one
+//      tie group);
+//   3. after one barrier every wave scans the histogram from the top, down to
+//      t* = max_w t_w (DPP prefix sums of counts and of the softmax mass
+//      count * exp((x - x_max) / T)): the k-th value tau, the mass of K and the
+//      top-p cutoff group.  Every entry >= t* was counted by its wave, so if
+//      the count reaches k at or above t* then tau is the exact k-th largest
+//      logit; otherwise the row takes the general body;
+//   4. when the kept set ends inside the tie group at tau, the lowest indices of
+//      that group are taken (rank by index inside the group);
+//   5. each wave compacts its members of P, draws their Philox noise and keeps
+//      its perturbed argmax; a block argmax picks the id.
+// Comparisons use the bf16 bit patterns as signed 16-bit integers: for positive
+// values that is the value order and every negative value sorts below them, so
+// it is exact whenever every t_w > +0.  Greedy rows take the first maximum.
+// Every other row -- no top-k, k > 1024, some t_w <= +0, NaN logits, a full
+// LDS segment, or fewer than k counted entries at or above t* -- runs the
+// general per-row body (general_row.hpp) on the same workgroup.
+#include "general_row.hpp"
+
+namespace tss {
+
+namespace {
+
+constexpr int kB = 1024;
+constexpr int kWv = kB / kWave;
+constexpr int kMaxK = 1024;
+constexpr int kSegV = 192;                 // candidate vectors per wave
+constexpr int kHistBins = 32768;           // one bin per positive bf16 bit pattern
+constexpr uint32_t kNegInfKey = 0x007Fu;
+constexpr uint32_t kPosInfKey = 0xFF80u;
+constexpr uint32_t kNegZeroKey = 0x7FFFu;
+constexpr uint32_t kPosZeroKey = 0x8000u;
+constexpr int32_t kPosInfBits = 0x7F80;    // bf16 +inf; larger positive patterns are NaN
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+struct FastShared {
+  uint32_t hist[kHistBins / 2];    // 16-bit counters, two per word (at most 16 * kSegV * 8 counts)
+  v4u cvec[kWv][kSegV];            // stored candidate vectors of each wave
+  uint32_t cvi[kWv][kSegV];        // their vector indices
+  int32_t cvm[kWv][kSegV];         // their maxima (bf16 bit patterns)
+  uint32_t pidx[kB];               // kept set P: indices
+  float pval[kB];                  //             logits
+  uint32_t ties[kB];
+  uint32_t wthr[kWv];              // per-wave thresholds (biased signed 16-bit order)
+  uint32_t wmax[kWv];              // per-wave maxima (same encoding)
+  uint32_t wcount[kWv];
+  float wz[kWv];
+  float ws[kWv];
+  int32_t wj[kWv];
+  uint32_t flag;                   // nonzero: the row takes the general body
+  int32_t tau_bits;                // scan results (wave 0)
+  int32_t vc_bits;
+  uint32_t need;
+  uint32_t n_eq;
+  float zp;
+  uint32_t scan_ok;
+  uint32_t nties;
+  uint32_t np;
+  uint32_t idx_cut;
+};
+
+union RowShared {
+  FastShared f;
+  general::Shared g;
+};
+
+// ---------------------------------------------------------------------------
+// bf16 helpers
+
+// Order keys of the two bf16 values packed in a dword (low half = lower index).
+__device__ __forceinline__ uint32_t keys2(uint32_t u) {
+  const uint32_t s = (u >> 15) & 0x00010001u;
+  return u ^ ((s * 0xFFFFu) | 0x80008000u);
+}
+
+__device__ __forceinline__ uint32_t canon_key(uint32_t k) {
+  return k == kNegZeroKey ? kPosZeroKey : k;
+}
+
+__device__ __forceinline__ uint32_t pk_max_i16(uint32_t a, uint32_t b) {
+  const i16x2 x = __builtin_bit_cast(i16x2, a);
+  const i16x2 y = __builtin_bit_cast(i16x2, b);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
+}
+
+__device__ __forceinline__ int32_t lo_i16(uint32_t u) { return (int32_t)(int16_t)(u & 0xFFFFu); }
+__device__ __forceinline__ int32_t hi_i16(uint32_t u) { return ((int32_t)u) >> 16; }
+
+// Largest of the eight bf16 bit patterns of a vector, as a signed 16-bit integer.
+__device__ __forceinline__ int32_t vec_max_i16(const v4u& d) {
+  const uint32_t m2 = pk_max_i16(pk_max_i16(d.x, d.y), pk_max_i16(d.z, d.w));
+  return max(lo_i16(m2), hi_i16(m2));
+}
+
+__device__ __forceinline__ uint32_t word_of(const v4u& d, int w) {
+  return w == 0 ? d.x : w == 1 ? d.y : w == 2 ? d.z : d.w;
+}
+
+__device__ __forceinline__ int32_t elem_i16(const v4u& d, int s) {
+  const uint32_t w = word_of(d, s >> 1);
+  return (s & 1) ? hi_i16(w) : lo_i16(w);
+}
+
+// Value of a positive bf16 bit pattern.
+__device__ __forceinline__ float bits_value(int32_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// ---------------------------------------------------------------------------
+// wave helpers
+
+// Inclusive prefix sum over the 64 lanes: DPP row shifts inside each row of 16
+// lanes, then row broadcasts of lanes 15 and 31.
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_scan_f32(float v) {
+  v += dpp_f<0x111, 0xF>(v);
+  v += dpp_f<0x112, 0xF>(v);
+  v += dpp_f<0x114, 0xF>(v);
+  v += dpp_f<0x118, 0xF>(v);
+  v += dpp_f<0x142, 0xA>(v);
+  v += dpp_f<0x143, 0xC>(v);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t lane_rank(unsigned long long m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Wave-wide max / min (result in every lane): DPP row shifts, row broadcasts,
+// then the last lane's value.
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
+__device__ __forceinline__ uint32_t wave_min_dpp(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x111, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x112, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x114, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x118, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x142, 0xA, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
+// c-th largest (c >= 1) of the wave's values, 0 standing for "no value" (the
+// result is 0 when fewer than c values exist).  Bitwise descent starting below
+// the leading bits shared by the largest and smallest value.
+template <int N>
+__device__ __forceinline__ uint32_t wave_cth_largest16(const uint32_t (&vals)[N], uint32_t c) {
+  uint32_t vmx = 0, vmn = 0xFFFFFFFFu, nnz = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    vmx = vals[i] > vmx ? vals[i] : vmx;
+    vmn = (vals[i] != 0 && vals[i] < vmn) ? vals[i] : vmn;
+    nnz += (uint32_t)__popcll(__ballot(vals[i] != 0));
+  }
+  if (nnz < c) return 0;
+  vmx = wave_max_dpp(vmx);
+  vmn = wave_min_dpp(vmn);
+  const uint32_t diff = vmx ^ vmn;
+  if (diff == 0) return vmx;
+  const int top = 31 - __builtin_clz(diff);
+  uint32_t prefix = vmx & ~((2u << top) - 1u);
+  for (int b = top; b >= 0; --b) {
+    const uint32_t trial = prefix | (1u << b);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) cnt += (uint32_t)__popcll(__ballot(vals[i] >= trial));
+    if (cnt >= c) prefix = trial;
+  }
+  return prefix;
+}
+
+struct Pick {
+  float z;
+  int32_t j;
+  float s;
+};
+
+__device__ __forceinline__ float wave_max_f32_dpp(float v) {
+  constexpr int kNegInf = (int)0xFF800000u;
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(v), 0x111, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(v), 0x112, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(v), 0x114, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(v), 0x118, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(v), 0x142, 0xA, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(v), 0x143, 0xC, 0xF, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+
+// Best (largest z, then smallest j) of the wave, returned in every lane.
+__device__ __forceinline__ Pick wave_pick(Pick p) {
+  const float zmax = wave_max_f32_dpp(p.z);
+  const bool top = p.z == zmax;
+  unsigned long long m = __ballot(top);
+  if (__popcll(m) > 1) {   // equal scores: the smallest index among them
+    const uint32_t jm = wave_min_dpp(top ? (uint32_t)p.j : 0xFFFFFFFFu);
+    m = __ballot(top && (uint32_t)p.j == jm);
+  }
+  const int sl = __ffsll((long long)m) - 1;
+  return Pick{zmax, __builtin_amdgcn_readlane(p.j, sl),
+              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p.s), sl))};
+}
+
+__device__ __forceinline__ Pick block_pick(Pick p, FastShared& fs) {
+  p = wave_pick(p);
+  const int wid = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    fs.wz[wid] = p.z;
+    fs.wj[wid] = p.j;
+    fs.ws[wid] = p.s;
+  }
+  __syncthreads();
+  Pick b{fs.wz[0], fs.wj[0], fs.ws[0]};
+#pragma unroll
+  for (int w = 1; w < kWv; ++w)
+    if (better(fs.wz[w], fs.wj[w], b.z, b.j)) b = Pick{fs.wz[w], fs.wj[w], fs.ws[w]};
+  return b;
+}
+
+__device__ __forceinline__ void write_result(const RowArgs& a, int r, int32_t id, float lp) {
+  a.out_ids[r] = id;
+  if (a.out_lp) a.out_lp[r] = lp;
+}
+
+// Greedy row: first index of the largest logit.
+template <int NV>
+__device__ __forceinline__ void greedy_row(const RowArgs& a, int r, int nvec, const v4u (&d)[NV],
+                                           FastShared& fs) {
+  uint32_t best = 0;
+  int32_t bj = 0x7FFFFFFF;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int32_t e0 = (i * kB + (int)threadIdx.x) * 8;
+    if (e0 >= nvec * 8) continue;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t k2 = keys2(word_of(d[i], w));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t k = canon_key(h ? (k2 >> 16) : (k2 & 0xFFFFu));
+        if (k > kPosInfKey) k = 0;   // NaN reads as -inf
+        const int32_t j = e0 + 2 * w + h;
+        if (k > best || (k == best && j < bj)) {
+          best = k;
+          bj = j;
+        }
+      }
+    }
+  }
+  const Pick p = block_pick(Pick{(float)best, bj, 0.0f}, fs);   // keys < 2^16 are exact in fp32
+  if (threadIdx.x == 0) {
+    if (p.z <= (float)kNegInfKey)
+      write_result(a, r, -1, __builtin_nanf(""));
+    else
+      write_result(a, r, p.j, 0.0f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// histogram of positive bf16 bit patterns, 16-bit counters packed two per word
+
+__device__ __forceinline__ void hist_add(uint32_t* hist, int32_t bits) {
+  atomicAdd(&hist[bits >> 1], 1u << ((bits & 1) * 16));
+}
+
+__device__ __forceinline__ uint32_t hist_get(const uint32_t* hist, int32_t bits) {
+  return (hist[bits >> 1] >> ((bits & 1) * 16)) & 0xFFFFu;
+}
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Result of the histogram scan (identical in every wave).
+struct ScanOut {
+  bool ok;            // false: fewer than k counted entries in [lo, hi]
+  int32_t tau_bits;   // the k-th value
+  uint32_t need;      // members of its tie group inside K (lowest indices)
+  uint32_t n_eq;      // size of that tie group
+  int32_t vc_bits;    // the top-p cutoff value (P = K and x >= cutoff)
+  float zp;           // mass of P in units of exp(x_max / T)
+};
+
+// Scan the bins [lo, hi] (bit patterns, hi = the row maximum) from the top.
+// Lane l takes bins top - 4l .. top - 4l - 3 of each 256-bin chunk.  When the
+// k-th value falls in the first chunk (the common case) the top-p cutoff is
+// found from the same registers; otherwise a second pass recomputes the masses.
+__device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, int32_t hi,
+                                             float inv_t, float m, uint32_t k, bool p_on,
+                                             float p) {
+  const int lane = threadIdx.x & (kWave - 1);
+  ScanOut o{false, 0, 0, 0, 0, 0.0f};
+  uint32_t cbase = 0, n_gt = 0;
+  float mbase = 0.0f, mass_gt = 0.0f, w_tau = 0.0f;
+  bool first = true, in_first = false;
+  uint32_t cc[4];
+  float mm[4], mx[4];   // count, mass, mass strictly above, per bin
+  for (int32_t top = hi; top >= lo; top -= 4 * kWave) {
+    uint32_t cs = 0;
+    float ms = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int32_t b = top - (4 * lane + i);
+      cc[i] = b >= lo ? hist_get(hist, b) : 0u;
+      mm[i] = cc[i] ? (float)cc[i] * __expf(__fmaf_rn(bits_value(b), inv_t, -m)) : 0.0f;
+      cs += cc[i];
+      ms += mm[i];
+    }
+    const uint32_t ci = wave_scan_u32(cs);
+    const float mi = wave_scan_f32(ms);
+    uint32_t cex = cbase + ci - cs;
+    float mex = mbase + mi - ms;
+    int32_t hit = -1;
+    uint32_t h_gt = 0, h_eq = 0;
+    float h_mgt = 0.0f, h_w = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mx[i] = mex;
+      if (hit < 0 && cc[i] && cex < k && cex + cc[i] >= k) {
+        hit = top - (4 * lane + i);
+        h_gt = cex;
+        h_eq = cc[i];
+        h_mgt = mex;
+        h_w = mm[i] / (float)cc[i];
+      }
+      cex += cc[i];
+      mex += mm[i];
+    }
+    const unsigned long long hm = __ballot(hit >= 0);
+    if (hm) {
+      const int sl = __ffsll((long long)hm) - 1;
+      o.ok = true;
+      o.tau_bits = __builtin_amdgcn_readlane(hit, sl);
+      n_gt = (uint32_t)__builtin_amdgcn_readlane((int)h_gt, sl);
+      o.n_eq = (uint32_t)__builtin_amdgcn_readlane((int)h_eq, sl);
+      mass_gt = readlane_f(h_mgt, sl);
+      w_tau = readlane_f(h_w, sl);
+      in_first = first;
+      break;
+    }
+    cbase += (uint32_t)__builtin_amdgcn_readlane((int)ci, kWave - 1);
+    mbase += readlane_f(mi, kWave - 1);
+    first = false;
+  }
+  if (!o.ok) return o;
+  o.need = k - n_gt;
+  const float zk = mass_gt + (float)o.need * w_tau;
+  o.vc_bits = o.tau_bits;
+  o.zp = zk;
+  if (!p_on) return o;
+  // the largest value whose K-mass from the top reaches p * Z_K
+  const float target = p * zk;
+  if (in_first) {
+    int32_t hit = -1;
+    float h_z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int32_t b = hi - (4 * lane + i);
+      const float mk = (b == o.tau_bits) ? zk : mx[i] + mm[i];
+      const bool ne = cc[i] != 0;
+      if (hit < 0 && b >= o.tau_bits && ne && mk >= target && (mx[i] < target || b == hi)) {
+        hit = b;
+        h_z = mk;
+      }
+    }
+    const unsigned long long hm = __ballot(hit >= 0);
+    if (hm) {
+      const int sl = __ffsll((long long)hm) - 1;
+      o.vc_bits = __builtin_amdgcn_readlane(hit, sl);
+      o.zp = readlane_f(h_z, sl);
+    }
+    return o;
+  }
+  float mb = 0.0f;
+  for (int32_t top = hi; top >= o.tau_bits; top -= 4 * kWave) {
+    bool ne[4];
+    float ms = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int32_t b = top - (4 * lane + i);
+      const uint32_t cnt = b > o.tau_bits ? hist_get(hist, b) : 0u;
+      ne[i] = cnt != 0 || b == o.tau_bits;
+      mm[i] = cnt ? (float)cnt * __expf(__fmaf_rn(bits_value(b), inv_t, -m)) : 0.0f;
+      ms += mm[i];
+    }
+    const float mi = wave_scan_f32(ms);
+    float mex = mb + mi - ms;
+    int32_t hit = -1;
+    float h_z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int32_t b = top - (4 * lane + i);
+      const float mk = (b == o.tau_bits) ? zk : mex + mm[i];
+      if (hit < 0 && b >= o.tau_bits && ne[i] && mk >= target && (mex < target || b == hi)) {
+        hit = b;
+        h_z = mk;
+      }
+      mex += mm[i];
+    }
+    const unsigned long long hm = __ballot(hit >= 0);
+    if (hm) {
+      const int sl = __ffsll((long long)hm) - 1;
+      o.vc_bits = __builtin_amdgcn_readlane(hit, sl);
+      o.zp = readlane_f(h_z, sl);
+      break;
+    }
+    mb += readlane_f(mi, kWave - 1);
+  }
+  return o;
+}
+
+template <int NV, int ROUTE>
+__global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
+  constexpr bool kHasK = (ROUTE == kRouteTopK || ROUTE == kRouteJoint);
+  constexpr bool kHasP = (ROUTE == kRouteTopP || ROUTE == kRouteJoint);
+  // threshold input: the first NB vectors, in groups of GV vectors (16 entries)
+  constexpr int NB = NV >= 2 ? NV / 2 : 1;
+  constexpr int GV = NB >= 2 ? 2 : 1;
+  constexpr int NG = NB / GV;
+  __shared__ RowShared sh;
+  FastShared& fs = sh.f;
+
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
+  const int64_t src = a.gather ? (int64_t)a.gather[r] : (int64_t)r;
+  const int64_t q = a.req_map ? (int64_t)a.req_map[r] : (int64_t)r;
+  const v4u* row = reinterpret_cast<const v4u*>(reinterpret_cast<const uint16_t*>(a.logits) +
+                                                src * a.row_stride);
+  const int nvec = (int)(a.vocab >> 3);
+  const float temp = a.temperature[q];
+  const int32_t kq = kHasK ? a.top_k[q] : 0;
+  const float pq = kHasP ? a.top_p[q] : 1.0f;
+  const uint64_t seed = a.seed[q];   // read up front: a late load would stall the tail
+  const bool greedy = !(temp >= 1e-5f);
+  const bool k_on = kHasK && kq >= 1 && (int64_t)kq < a.vocab;
+  const bool p_on = kHasP && pq < 1.0f - 1e-6f;
+
+  // Rows without top-k draw noise for every entry (VALU-bound: nothing to gain
+  // from register residency), and k above kMaxK: general body.
+  if (!greedy && (!k_on || kq > kMaxK)) {
+    general::general_row<uint16_t, ROUTE, kOutSample>(a, r, sh.g);
+    return;
+  }
+
+  // ---- stream the whole row into registers.  Slots past the row re-read its
+  // last vector and are ignored where used, so every load is unconditional and
+  // each vector is waited for on its own at its first use.
+  v4u d[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int vi = i * kB + tid;
+    d[i] = __builtin_nontemporal_load(row + (vi < nvec ? vi : nvec - 1));
+  }
+  if (greedy) {
+    greedy_row<NV>(a, r, nvec, d, fs);
+    return;
+  }
+
+  // clear the histogram while the loads are in flight
+  {
+    v4u* h4 = reinterpret_cast<v4u*>(fs.hist);
+#pragma unroll
+    for (int i = 0; i < kHistBins / 8 / kB; ++i) h4[i * kB + tid] = v4u{0u, 0u, 0u, 0u};
+    if (tid == 0) {
+      fs.flag = 0;
+      fs.nties = 0;
+      fs.np = 0;
+      fs.idx_cut = 0xFFFFFFFFu;
+    }
+  }
+  __syncthreads();
+
+  // ---- 1. this wave's threshold, from the first half of its data
+  int32_t vmax = -32768;           // running maximum bit pattern (signed 16-bit order)
+  int32_t vm[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    vm[i] = (i * kB + tid < nvec) ? vec_max_i16(d[i]) : -32768;
+    vmax = max(vmax, vm[i]);
+  }
+  uint32_t gm[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    int32_t mg = vm[g * GV];
+#pragma unroll
+    for (int v = 1; v < GV; ++v) mg = max(mg, vm[g * GV + v]);
+    gm[g] = (uint32_t)(mg + 0x8000);           // unsigned image of the signed order
+  }
+  const uint32_t c16 = ((uint32_t)kq + kWv - 1) / kWv + 4;
+  const uint32_t c = (uint32_t)kq < c16 ? (uint32_t)kq : c16;
+  const uint32_t tw = wave_cth_largest16<NG>(gm, c);
+  const int32_t t16 = (int32_t)tw - 0x8000;
+  const bool wave_ok = t16 > 0;    // the signed order is the value order only above +0
+  if (lane == 0) {
+    fs.wthr[wid] = tw;
+    if (!wave_ok) fs.flag = 1;
+  }
+
+  // ---- 2. filter vectors into this wave's segment; count entries >= t16
+  uint32_t wfill = 0;               // wave-uniform number of vectors offered
+  uint32_t counted = 0;             // stored vectors already counted
+  v4u* my_vec = fs.cvec[wid];
+  uint32_t* my_vi = fs.cvi[wid];
+  int32_t* my_vm = fs.cvm[wid];
+  auto count_stored = [&](uint32_t from, uint32_t to) {
+    // the wave reads vectors other lanes of the same wave have just written
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (uint32_t e = from + lane; e < to; e += kWave) {
+      const v4u dv = my_vec[e];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int32_t val = elem_i16(dv, s);
+        if (val >= t16) hist_add(fs.hist, val);
+      }
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    int32_t mv;
+    if (i < NB) {
+      mv = vm[i];
+    } else {
+      mv = (i * kB + tid < nvec) ? vec_max_i16(d[i]) : -32768;
+      vmax = max(vmax, mv);
+    }
+    const bool cand = wave_ok && mv >= t16;
+    const unsigned long long bm = __ballot(cand);
+    if (bm) {
+      if (cand) {
+        const uint32_t pos = wfill + lane_rank(bm);
+        if (pos < (uint32_t)kSegV) {
+          my_vec[pos] = d[i];
+          my_vi[pos] = (uint32_t)(i * kB + tid);
+          my_vm[pos] = mv;
+        } else {
+          fs.flag = 1;
+        }
+      }
+      wfill += (uint32_t)__popcll(bm);
+    }
+    if (i == NB - 1 && NB < NV) {     // count the first half while the rest streams in
+      const uint32_t to = wfill < (uint32_t)kSegV ? wfill : (uint32_t)kSegV;
+      count_stored(0, to);
+      counted = to;
+    }
+  }
+  const uint32_t stored = wfill < (uint32_t)kSegV ? wfill : (uint32_t)kSegV;
+  count_stored(counted, stored);
+  const uint32_t wmaxu = wave_max_dpp((uint32_t)(vmax + 0x8000));
+  if (lane == 0) {
+    fs.wcount[wid] = stored;
+    fs.wmax[wid] = wmaxu;
+  }
+  __syncthreads();
+
+  // ---- 3. scan the histogram from the row maximum down to t* = max_w t_w
+  uint32_t kmaxu = 0, tstaru = 0;
+#pragma unroll
+  for (int w = 0; w < kWv; ++w) {
+    kmaxu = fs.wmax[w] > kmaxu ? fs.wmax[w] : kmaxu;
+    tstaru = fs.wthr[w] > tstaru ? fs.wthr[w] : tstaru;
+  }
+  const int32_t kmax16 = (int32_t)kmaxu - 0x8000;
+  const int32_t tstar16 = (int32_t)tstaru - 0x8000;
+  const float inv_t = 1.0f / temp;
+  const float m = __fmul_rn(bits_value(kmax16), inv_t);
+  const bool usable = fs.flag == 0 && kmax16 <= kPosInfBits;   // no NaN, no full segment
+  if (wid == 0) {
+    ScanOut so{false, 0, 0, 0, 0, 0.0f};
+    if (usable) so = scan_hist(fs.hist, tstar16, kmax16, inv_t, m, (uint32_t)kq, p_on, pq);
+    if (lane == 0) {
+      fs.scan_ok = so.ok ? 1u : 0u;
+      fs.tau_bits = so.tau_bits;
+      fs.vc_bits = so.vc_bits;
+      fs.need = so.need;
+      fs.n_eq = so.n_eq;
+      fs.zp = so.zp;
+    }
+  }
+  __syncthreads();
+  if (fs.scan_ok == 0) {
+    __syncthreads();
+    general::general_row<uint16_t, ROUTE, kOutSample>(a, r, sh.g);
+    return;
+  }
+  ScanOut o{true, fs.tau_bits, fs.need, fs.n_eq, fs.vc_bits, fs.zp};
+  const uint32_t stored_mine = fs.wcount[wid];
+
+  // ---- 4. lowest indices of the boundary tie group, when P reaches into it
+  uint32_t idx_cut = 0xFFFFFFFFu;
+  if (o.vc_bits == o.tau_bits && o.need < o.n_eq) {
+    for (uint32_t e = lane; e < stored_mine; e += kWave) {
+      const v4u dv = my_vec[e];
+      const uint32_t vi = my_vi[e];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        if (elem_i16(dv, s) == o.tau_bits) {
+          const uint32_t slot = atomicAdd(&fs.nties, 1u);
+          if (slot < (uint32_t)kB) fs.ties[slot] = vi * 8 + (uint32_t)s;
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t nt = fs.nties;
+    if (nt > (uint32_t)kB) {
+      __syncthreads();
+      general::general_row<uint16_t, ROUTE, kOutSample>(a, r, sh.g);
+      return;
+    }
+    if ((uint32_t)tid < nt) {
+      const uint32_t mine = fs.ties[tid];
+      uint32_t rank = 0;
+      for (uint32_t t = 0; t < nt; ++t) rank += fs.ties[t] < mine ? 1u : 0u;
+      if (rank == o.need - 1) fs.idx_cut = mine;
+    }
+    __syncthreads();
+    idx_cut = fs.idx_cut;
+  }
+
+  // ---- 5. compact P over all waves (vector maxima first, one atomic per
+  // wave), then Philox noise for P only and a block argmax
+  constexpr int kChunks = (kSegV + kWave - 1) / kWave;
+  {
+    uint32_t vsel = 0;      // chunks whose vector holds a member of P (bit per chunk)
+#pragma unroll
+    for (int ch = 0; ch < kChunks; ++ch) {
+      const uint32_t e = (uint32_t)(ch * kWave + lane);
+      if (e < stored_mine && my_vm[e] >= o.vc_bits) vsel |= 1u << ch;
+    }
+    uint32_t masks[kChunks];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int ch = 0; ch < kChunks; ++ch) {
+      masks[ch] = 0;
+      if (__ballot((vsel >> ch) & 1u) == 0) continue;
+      if ((vsel >> ch) & 1u) {
+        const uint32_t e = (uint32_t)(ch * kWave + lane);
+        const v4u dv = my_vec[e];
+        const uint32_t vi = my_vi[e];
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+          const int32_t val = elem_i16(dv, sl);
+          const uint32_t j = vi * 8 + (uint32_t)sl;
+          masks[ch] |= (uint32_t)(val >= o.vc_bits && (val > o.tau_bits || j <= idx_cut)) << sl;
+        }
+        cnt += (uint32_t)__popc(masks[ch]);
+      }
+    }
+    const uint32_t incl = wave_scan_u32(cnt);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+    if (total != 0) {
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&fs.np, total);
+      base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+      uint32_t pos = base + incl - cnt;
+#pragma unroll
+      for (int ch = 0; ch < kChunks; ++ch) {
+        uint32_t mask = masks[ch];
+        if (!mask) continue;
+        const uint32_t e = (uint32_t)(ch * kWave + lane);
+        const v4u dv = my_vec[e];
+        const uint32_t vi = my_vi[e];
+        while (mask) {
+          const int sl = __ffs(mask) - 1;
+          mask &= mask - 1;
+          if (pos < (uint32_t)kB) {
+            fs.pidx[pos] = vi * 8 + (uint32_t)sl;
+            fs.pval[pos] = bits_value(elem_i16(dv, sl));
+          }
+          ++pos;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t np = fs.np < (uint32_t)kB ? fs.np : (uint32_t)kB;
+  Pick best{-__builtin_inff(), 0x7FFFFFFF, 0.0f};
+  if ((uint32_t)(wid * kWave) < np) {
+    if ((uint32_t)tid < np) {
+      const NoiseStream ns{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
+                           (uint32_t)a.step_offset, (uint32_t)(a.step_offset >> 32)};
+      const uint32_t j = fs.pidx[tid];
+      const float sv = __fmul_rn(fs.pval[tid], inv_t);
+      best = Pick{sv + gumbel_from_word(ns.word(j)), (int32_t)j, sv};
+    }
+  }
+  best = block_pick(best, fs);
+  if (tid == 0) write_result(a, r, best.j, (float)((double)best.s - (double)m - log((double)o.zp)));
+}
+
+template <int NV>
+hipError_t launch_nv(const RowArgs& a, Route route, hipStream_t stream) {
+  const dim3 grid(a.n), block(kB);
+  switch (route) {
+    case kRouteNone:
+      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteNone>), grid, block, 0, stream, a);
+      break;
+    case kRouteTopK:
+      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteTopK>), grid, block, 0, stream, a);
+      break;
+    case kRouteTopP:
+      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteTopP>), grid, block, 0, stream, a);
+      break;
+    default:
+      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteJoint>), grid, block, 0, stream, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rows(const RowArgs& a, DType dtype, Route route, OutMode mode,
+                       hipStream_t stream) {
+  if (a.n <= 0) return hipSuccess;
+  const bool aligned = (reinterpret_cast<uintptr_t>(a.logits) % 16) == 0 && (a.row_stride % 8) == 0;
+  const int64_t nvec = a.vocab / 8;
+  if (dtype == kBF16 && mode == kOutSample && route != kRouteTopP && aligned &&
+      (a.vocab % 8) == 0 && nvec <= 16 * (int64_t)kB) {
+    const int64_t per = (nvec + kB - 1) / kB;
+    if (per <= 1) return launch_nv<1>(a, route, stream);
+    if (per <= 2) return launch_nv<2>(a, route, stream);
+    if (per <= 4) return launch_nv<4>(a, route, stream);
+    if (per <= 8) return launch_nv<8>(a, route, stream);
+    return launch_nv<16>(a, route, stream);
+  }
+  return launch_rows_general(a, dtype, route, mode, stream);
+}
+
+}  // namespace tss
