@@ -15,6 +15,7 @@ stream) and the CPU oracle's rate on a bounded sample of the same rows.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -105,10 +106,32 @@ def main():
     ids = torch.empty(wl.n, dtype=torch.int32, device=dev)
     lps = torch.empty(wl.n, dtype=torch.float32, device=dev)
 
-    def step(i):
+    def step_checked(i):
         sampler.sample(logits[i % copies], wl.n, params, no_top_k=wl.no_top_k,
                        no_top_p=wl.no_top_p, gather_indices=gather, token_to_request_index=req,
                        step_offset=i, output=ids, logprob_output=lps)
+
+    # Timed steps call the C ABI directly with argument lists built once, so
+    # the host issues a step in a few microseconds and the GPU never waits on
+    # Python; the checked wrapper above runs the warm-up steps.
+    lib = tsa.library()
+    prm = params._struct(dev)
+    prm_ref = ctypes.byref(prm)
+    stream_ptr = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    dt_code = tsa.TS_F32 if wl.logits.dtype == torch.float32 else tsa.TS_BF16
+    call_args = [[sampler._h, ctypes.c_void_p(lg.data_ptr()), dt_code, lg.shape[0], lg.stride(0),
+                  wl.n, None if gather is None else ctypes.c_void_p(gather.data_ptr()),
+                  None if req is None else ctypes.c_void_p(req.data_ptr()), prm_ref, 0,
+                  int(wl.no_top_k), int(wl.no_top_p), ctypes.c_void_p(ids.data_ptr()),
+                  ctypes.c_void_p(lps.data_ptr()), stream_ptr] for lg in logits]
+    ts_sample = lib.ts_sample
+
+    def step(i):
+        cargs = call_args[i % copies]
+        cargs[9] = i
+        st = ts_sample(*cargs)
+        if st != tsa.TS_OK:
+            raise RuntimeError(f"ts_sample failed with status {st}")
 
     if args.copy_probe_mb:
         a = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
@@ -118,7 +141,7 @@ def main():
         torch.cuda.synchronize()
 
     for i in range(args.warmup):
-        step(i)
+        (step_checked if i < 2 else step)(i)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)       # the stream ts_sample launches on

@@ -238,6 +238,7 @@ __device__ __forceinline__ Pick wave_pick(Pick p) {
               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p.s), sl))};
 }
 
+// Block-wide best; the result is meaningful in wave 0 only.
 __device__ __forceinline__ Pick block_pick(Pick p, FastShared& fs) {
   p = wave_pick(p);
   const int wid = threadIdx.x / kWave;
@@ -247,10 +248,12 @@ __device__ __forceinline__ Pick block_pick(Pick p, FastShared& fs) {
     fs.ws[wid] = p.s;
   }
   __syncthreads();
-  Pick b{fs.wz[0], fs.wj[0], fs.ws[0]};
-#pragma unroll
-  for (int w = 1; w < kWv; ++w)
-    if (better(fs.wz[w], fs.wj[w], b.z, b.j)) b = Pick{fs.wz[w], fs.wj[w], fs.ws[w]};
+  Pick b{-__builtin_inff(), 0x7FFFFFFF, 0.0f};
+  if (wid == 0) {
+    const int l = threadIdx.x & (kWave - 1);
+    if (l < kWv) b = Pick{fs.wz[l], fs.wj[l], fs.ws[l]};
+    b = wave_pick(b);
+  }
   return b;
 }
 
@@ -514,7 +517,8 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   int32_t vm[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    vm[i] = (i * kB + tid < nvec) ? vec_max_i16(d[i]) : -32768;
+    vm[i] = vec_max_i16(d[i]);
+    if ((i + 1) * kB > nvec) vm[i] = (i * kB + tid < nvec) ? vm[i] : -32768;   // wave-uniform test
     vmax = max(vmax, vm[i]);
   }
   uint32_t gm[NG];
@@ -561,21 +565,18 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
     if (i < NB) {
       mv = vm[i];
     } else {
-      mv = (i * kB + tid < nvec) ? vec_max_i16(d[i]) : -32768;
+      mv = vec_max_i16(d[i]);
+      if ((i + 1) * kB > nvec) mv = (i * kB + tid < nvec) ? mv : -32768;   // block-uniform test
       vmax = max(vmax, mv);
     }
     const bool cand = wave_ok && mv >= t16;
     const unsigned long long bm = __ballot(cand);
     if (bm) {
-      if (cand) {
-        const uint32_t pos = wfill + lane_rank(bm);
-        if (pos < (uint32_t)kSegV) {
-          my_vec[pos] = d[i];
-          my_vi[pos] = (uint32_t)(i * kB + tid);
-          my_vm[pos] = mv;
-        } else {
-          fs.flag = 1;
-        }
+      const uint32_t pos = wfill + lane_rank(bm);
+      if (cand && pos < (uint32_t)kSegV) {
+        my_vec[pos] = d[i];
+        my_vi[pos] = (uint32_t)(i * kB + tid);
+        my_vm[pos] = mv;
       }
       wfill += (uint32_t)__popcll(bm);
     }
@@ -585,6 +586,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
       counted = to;
     }
   }
+  if (lane == 0 && wfill > (uint32_t)kSegV) fs.flag = 1;   // a full segment lost vectors
   const uint32_t stored = wfill < (uint32_t)kSegV ? wfill : (uint32_t)kSegV;
   count_stored(counted, stored);
   const uint32_t wmaxu = wave_max_dpp((uint32_t)(vmax + 0x8000));
@@ -631,6 +633,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   uint32_t idx_cut = 0xFFFFFFFFu;
   if (o.vc_bits == o.tau_bits && o.need < o.n_eq) {
     for (uint32_t e = lane; e < stored_mine; e += kWave) {
+      if (my_vm[e] < o.tau_bits) continue;
       const v4u dv = my_vec[e];
       const uint32_t vi = my_vi[e];
 #pragma unroll
