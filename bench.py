@@ -47,6 +47,29 @@ def logits_bytes(wl) -> int:
     return wl.n * wl.vocab * wl.logits.element_size()
 
 
+def algorithmic_bytes(wl) -> int:
+    """HBM bytes one step must move: every selected logit read once, plus per
+    row its gather and request indices, the request's parameters (T 4 B, k 4 B,
+    p 4 B, seed 8 B) and the outputs (id 4 B, log-prob 4 B)."""
+    per_row = 4 + 8 + 8
+    per_row += 0 if wl.no_top_k else 4
+    per_row += 0 if wl.no_top_p else 4
+    per_row += 0 if wl.gather_indices is None else 4
+    per_row += 0 if wl.token_to_request_index is None else 4
+    return logits_bytes(wl) + wl.n * per_row
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summaries, or None when
+    none matches this workload and the current kernel sources."""
+    from token_sampling_scaled_amd import profiling
+    digest = profiling.source_digest()
+    for rec in profiling.read_records(os.path.join(ROOT, "profiles")):
+        if rec.get("workload") == workload and rec.get("source_sha256") == digest:
+            return rec["bytes_per_launch"]
+    return None
+
+
 def cpu_baseline(wl, budget_s: float):
     """The fp64 oracle, single process, on the leading rows of the same workload."""
     import oracle
@@ -94,7 +117,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     wl = synth.make(args.workload)
-    nbytes = logits_bytes(wl)
+    nbytes = algorithmic_bytes(wl)
     buf_bytes = wl.logits.numel() * wl.logits.element_size()
     copies = args.copies or max(2, int(np.ceil(400e6 / buf_bytes)))
     logits = [wl.logits.to(dev) for _ in range(copies)]
@@ -158,7 +181,7 @@ def main():
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
 
     rows_per_s = wl.n * args.steps / wall
-    gbps = nbytes * args.steps / wall / 1e9
+    gbps = logits_bytes(wl) * args.steps / wall / 1e9
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     out = {
         "metric": METRIC,
@@ -178,9 +201,10 @@ def main():
         "config": {"workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}",
                    "rows": wl.n, "vocab": wl.vocab, "logits_dtype": str(wl.logits.dtype).split(".")[-1],
                    "route": ["none", "top-k", "top-p", "joint"][tsa.select_route(wl.no_top_k, wl.no_top_p)],
-                   "input_copies": copies, "logits_bytes_per_step": nbytes},
+                   "input_copies": copies, "logits_bytes_per_step": logits_bytes(wl),
+                   "algorithmic_bytes_per_step": nbytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(args.workload),
                      "kernel_ms_per_launch": kernel_ms},
     }
     if not args.no_cpu_baseline:
