@@ -1,29 +1,33 @@
 // Register-resident sampling kernel for bf16 rows (vocab <= 131072, vocab a
 // multiple of 8, rows 16-byte aligned): one workgroup of 1024 threads (16
 // waves) per output row; every logit is read from HBM exactly once with
-// non-temporal 16-byte loads, all issued up front, and kept in VGPRs.
+// non-temporal 16-byte loads and kept in VGPRs.
 //
 // Rows with an active top-k (k <= 1024), with or without top-p.  The waves
 // work independently while the row streams in -- data reaches the 16 waves of
 // a workgroup at very different times, so no step waits for another wave until
 // the row has arrived:
-//   1. threshold: from the first half of its own data, wave w takes
-//      t_w = the c-th largest of its 16-entry group maxima (bitwise descent with
-//      ballots), c = min(k, ceil(k/16) + 4);
+//   1. threshold: each wave issues the loads of the first half of its data,
+//      then issues each load of the second half as a first-half vector
+//      arrives (a wave blocked on a load issue could not work on data it
+//      already holds), and takes t_w = the c-th largest of its 16-entry group
+//      maxima over the first half (bitwise descent with ballots),
+//      c = min(k, ceil(k/16) + 4);
 //   2. filter: a 16-byte vector whose maximum reaches t_w is copied whole into
 //      the wave's LDS segment (ballot + mbcnt), and its entries >= t_w are
 //      counted in a histogram with one bin per bf16 value (a bin is exactly one
 //      tie group);
-//   3. after one barrier every wave scans the histogram from the top, down to
+//   3. after one barrier wave 0 scans the histogram from the top, down to
 //      t* = max_w t_w (DPP prefix sums of counts and of the softmax mass
 //      count * exp((x - x_max) / T)): the k-th value tau, the mass of K and the
 //      top-p cutoff group.  Every entry >= t* was counted by its wave, so if
 //      the count reaches k at or above t* then tau is the exact k-th largest
 //      logit; otherwise the row takes the general body;
-//   4. when the kept set ends inside the tie group at tau, the lowest indices of
-//      that group are taken (rank by index inside the group);
-//   5. each wave compacts its members of P, draws their Philox noise and keeps
-//      its perturbed argmax; a block argmax picks the id.
+//   4. when the kept set ends inside the tie group at tau, the members of that
+//      group are published and each one is ranked by index (one barrier);
+//   5. the members of P are compacted over all waves (one atomic per wave);
+//      Philox noise is drawn for P only -- by one wave when |P| <= 64, else one
+//      member per thread -- and the perturbed argmax picks the id.
 // Comparisons use the bf16 bit patterns as signed 16-bit integers: for positive
 // values that is the value order and every negative value sorts below them, so
 // it is exact whenever every t_w > +0.  Greedy rows take the first maximum.
@@ -39,7 +43,8 @@ namespace {
 constexpr int kB = 1024;
 constexpr int kWv = kB / kWave;
 constexpr int kMaxK = 1024;
-constexpr int kSegV = 192;                 // candidate vectors per wave
+constexpr int kSegV = 224;                 // candidate vectors per wave
+constexpr int kMaxTies = 1024;             // published members of the boundary tie group
 constexpr int kHistBins = 32768;           // one bin per positive bf16 bit pattern
 constexpr uint32_t kNegInfKey = 0x007Fu;
 constexpr uint32_t kPosInfKey = 0xFF80u;
@@ -53,11 +58,11 @@ typedef short i16x2 __attribute__((ext_vector_type(2)));
 struct FastShared {
   uint32_t hist[kHistBins / 2];    // 16-bit counters, two per word (at most 16 * kSegV * 8 counts)
   v4u cvec[kWv][kSegV];            // stored candidate vectors of each wave
-  uint32_t cvi[kWv][kSegV];        // their vector indices
-  int32_t cvm[kWv][kSegV];         // their maxima (bf16 bit patterns)
-  uint32_t pidx[kB];               // kept set P: indices
-  float pval[kB];                  //             logits
-  uint32_t ties[kB];
+  uint32_t cvim[kWv][kSegV];       // their vector index (i * 1024 + tid < 2^14, low half)
+                                   // and maximum (bf16 bit pattern, high half)
+  uint32_t pidx[kMaxK];            // kept set P: indices (each wave a range of its own)
+  float pval[kMaxK];               //             logits
+  uint32_t ties[kMaxTies];         // indices of the boundary tie group
   uint32_t wthr[kWv];              // per-wave thresholds (biased signed 16-bit order)
   uint32_t wmax[kWv];              // per-wave maxima (same encoding)
   uint32_t wcount[kWv];
@@ -73,7 +78,6 @@ struct FastShared {
   uint32_t scan_ok;
   uint32_t nties;
   uint32_t np;
-  uint32_t idx_cut;
 };
 
 union RowShared {
@@ -321,47 +325,55 @@ struct ScanOut {
   float zp;           // mass of P in units of exp(x_max / T)
 };
 
+// Softmax weight exp(x / T - m) of the positive bf16 pattern b.
+__device__ __forceinline__ float bin_weight(int32_t b, float inv_t, float m) {
+  return __expf(__fmaf_rn(bits_value(b), inv_t, -m));
+}
+
 // Scan the bins [lo, hi] (bit patterns, hi = the row maximum) from the top.
 // Lane l takes bins top - 4l .. top - 4l - 3 of each 256-bin chunk.  When the
 // k-th value falls in the first chunk (the common case) the top-p cutoff is
 // found from the same registers; otherwise a second pass recomputes the masses.
+// The cutoff group is the first one, from the top, whose cumulative K-mass
+// reaches p * Z_K; the top group is always kept.
 __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, int32_t hi,
                                              float inv_t, float m, uint32_t k, bool p_on,
                                              float p) {
   const int lane = threadIdx.x & (kWave - 1);
   ScanOut o{false, 0, 0, 0, 0, 0.0f};
   uint32_t cbase = 0, n_gt = 0;
-  float mbase = 0.0f, mass_gt = 0.0f, w_tau = 0.0f;
-  bool first = true, in_first = false;
+  float mbase = 0.0f, mass_gt = 0.0f;
+  bool in_first = true;
   uint32_t cc[4];
-  float mm[4], mx[4];   // count, mass, mass strictly above, per bin
+  float mm[4], mx[4];   // per bin: count, mass, mass of the bins above it
   for (int32_t top = hi; top >= lo; top -= 4 * kWave) {
     uint32_t cs = 0;
     float ms = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int32_t b = top - (4 * lane + i);
-      cc[i] = b >= lo ? hist_get(hist, b) : 0u;
-      mm[i] = cc[i] ? (float)cc[i] * __expf(__fmaf_rn(bits_value(b), inv_t, -m)) : 0.0f;
+      const uint32_t h = hist_get(hist, b > 0 ? b : 0);   // unconditional: the reads overlap
+      cc[i] = b >= lo ? h : 0u;
+      const float w = bin_weight(b, inv_t, m);
+      mm[i] = cc[i] ? (float)cc[i] * w : 0.0f;
       cs += cc[i];
       ms += mm[i];
     }
     const uint32_t ci = wave_scan_u32(cs);
     const float mi = wave_scan_f32(ms);
     uint32_t cex = cbase + ci - cs;
-    float mex = mbase + mi - ms;
+    float mex = mbase + (mi - ms);
     int32_t hit = -1;
     uint32_t h_gt = 0, h_eq = 0;
-    float h_mgt = 0.0f, h_w = 0.0f;
+    float h_mgt = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       mx[i] = mex;
-      if (hit < 0 && cc[i] && cex < k && cex + cc[i] >= k) {
+      if (cex < k && cex + cc[i] >= k) {   // at most one bin of the row crosses k
         hit = top - (4 * lane + i);
         h_gt = cex;
         h_eq = cc[i];
         h_mgt = mex;
-        h_w = mm[i] / (float)cc[i];
       }
       cex += cc[i];
       mex += mm[i];
@@ -374,21 +386,18 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
       n_gt = (uint32_t)__builtin_amdgcn_readlane((int)h_gt, sl);
       o.n_eq = (uint32_t)__builtin_amdgcn_readlane((int)h_eq, sl);
       mass_gt = readlane_f(h_mgt, sl);
-      w_tau = readlane_f(h_w, sl);
-      in_first = first;
       break;
     }
     cbase += (uint32_t)__builtin_amdgcn_readlane((int)ci, kWave - 1);
     mbase += readlane_f(mi, kWave - 1);
-    first = false;
+    in_first = false;
   }
   if (!o.ok) return o;
   o.need = k - n_gt;
-  const float zk = mass_gt + (float)o.need * w_tau;
+  const float zk = mass_gt + (float)o.need * bin_weight(o.tau_bits, inv_t, m);
   o.vc_bits = o.tau_bits;
   o.zp = zk;
   if (!p_on) return o;
-  // the largest value whose K-mass from the top reaches p * Z_K
   const float target = p * zk;
   if (in_first) {
     int32_t hit = -1;
@@ -396,11 +405,11 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int32_t b = hi - (4 * lane + i);
-      const float mk = (b == o.tau_bits) ? zk : mx[i] + mm[i];
-      const bool ne = cc[i] != 0;
-      if (hit < 0 && b >= o.tau_bits && ne && mk >= target && (mx[i] < target || b == hi)) {
+      const float cum = (b == o.tau_bits) ? zk : mx[i] + mm[i];
+      if (hit < 0 && b >= o.tau_bits && cc[i] != 0 && cum >= target &&
+          (mx[i] < target || b == hi)) {
         hit = b;
-        h_z = mk;
+        h_z = cum;
       }
     }
     const unsigned long long hm = __ballot(hit >= 0);
@@ -418,22 +427,24 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int32_t b = top - (4 * lane + i);
-      const uint32_t cnt = b > o.tau_bits ? hist_get(hist, b) : 0u;
+      const uint32_t h = hist_get(hist, b > 0 ? b : 0);
+      const uint32_t cnt = b > o.tau_bits ? h : 0u;
       ne[i] = cnt != 0 || b == o.tau_bits;
-      mm[i] = cnt ? (float)cnt * __expf(__fmaf_rn(bits_value(b), inv_t, -m)) : 0.0f;
+      const float w = bin_weight(b, inv_t, m);
+      mm[i] = cnt ? (float)cnt * w : 0.0f;
       ms += mm[i];
     }
     const float mi = wave_scan_f32(ms);
-    float mex = mb + mi - ms;
+    float mex = mb + (mi - ms);
     int32_t hit = -1;
     float h_z = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int32_t b = top - (4 * lane + i);
-      const float mk = (b == o.tau_bits) ? zk : mex + mm[i];
-      if (hit < 0 && b >= o.tau_bits && ne[i] && mk >= target && (mex < target || b == hi)) {
+      const float cum = (b == o.tau_bits) ? zk : mex + mm[i];
+      if (hit < 0 && b >= o.tau_bits && ne[i] && cum >= target && (mex < target || b == hi)) {
         hit = b;
-        h_z = mk;
+        h_z = cum;
       }
       mex += mm[i];
     }
@@ -447,6 +458,26 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
     mb += readlane_f(mi, kWave - 1);
   }
   return o;
+}
+
+// The wave's lanes read LDS entries other lanes of the same wave have just
+// written.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Number of published tie-group indices below j.
+__device__ __forceinline__ uint32_t tie_rank(const uint32_t* ties, uint32_t nt, uint32_t j) {
+  uint32_t rank = 0;
+  const v4u* t4 = reinterpret_cast<const v4u*>(ties);
+  for (uint32_t t = 0; t < nt; t += 4) {
+    const v4u v = t4[t >> 2];
+    rank += (v.x < j ? 1u : 0u) + ((t + 1 < nt && v.y < j) ? 1u : 0u) +
+            ((t + 2 < nt && v.z < j) ? 1u : 0u) + ((t + 3 < nt && v.w < j) ? 1u : 0u);
+  }
+  return rank;
 }
 
 template <int NV, int ROUTE>
@@ -484,19 +515,26 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
     return;
   }
 
-  // ---- stream the whole row into registers.  Slots past the row re-read its
-  // last vector and are ignored where used, so every load is unconditional and
-  // each vector is waited for on its own at its first use.
+  // ---- stream the row into registers.  Slots past the row re-read its last
+  // vector and are ignored where used, so every load is unconditional and
+  // each vector is waited for on its own at its first use.  The first half is
+  // issued now, the second half one load per arriving first-half vector.
   v4u d[NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
+  for (int i = 0; i < NB; ++i) {
     const int vi = i * kB + tid;
     d[i] = __builtin_nontemporal_load(row + (vi < nvec ? vi : nvec - 1));
   }
   if (greedy) {
+#pragma unroll
+    for (int i = NB; i < NV; ++i) {
+      const int vi = i * kB + tid;
+      d[i] = __builtin_nontemporal_load(row + (vi < nvec ? vi : nvec - 1));
+    }
     greedy_row<NV>(a, r, nvec, d, fs);
     return;
   }
+  const float inv_t = 1.0f / temp;
 
   // clear the histogram while the loads are in flight
   {
@@ -507,7 +545,6 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
       fs.flag = 0;
       fs.nties = 0;
       fs.np = 0;
-      fs.idx_cut = 0xFFFFFFFFu;
     }
   }
   __syncthreads();
@@ -517,9 +554,14 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   int32_t vm[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    vm[i] = vec_max_i16(d[i]);
-    if ((i + 1) * kB > nvec) vm[i] = (i * kB + tid < nvec) ? vm[i] : -32768;   // wave-uniform test
+    vm[i] = tid < nvec - i * kB ? vec_max_i16(d[i]) : -32768;
     vmax = max(vmax, vm[i]);
+    if (NB + i < NV) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int vi = (NB + i) * kB + tid;
+      d[NB + i] = __builtin_nontemporal_load(row + (vi < nvec ? vi : nvec - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   uint32_t gm[NG];
 #pragma unroll
@@ -543,13 +585,9 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   uint32_t wfill = 0;               // wave-uniform number of vectors offered
   uint32_t counted = 0;             // stored vectors already counted
   v4u* my_vec = fs.cvec[wid];
-  uint32_t* my_vi = fs.cvi[wid];
-  int32_t* my_vm = fs.cvm[wid];
+  uint32_t* my_vim = fs.cvim[wid];
   auto count_stored = [&](uint32_t from, uint32_t to) {
-    // the wave reads vectors other lanes of the same wave have just written
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_lds_sync();
     for (uint32_t e = from + lane; e < to; e += kWave) {
       const v4u dv = my_vec[e];
 #pragma unroll
@@ -565,8 +603,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
     if (i < NB) {
       mv = vm[i];
     } else {
-      mv = vec_max_i16(d[i]);
-      if ((i + 1) * kB > nvec) mv = (i * kB + tid < nvec) ? mv : -32768;   // block-uniform test
+      mv = tid < nvec - i * kB ? vec_max_i16(d[i]) : -32768;
       vmax = max(vmax, mv);
     }
     const bool cand = wave_ok && mv >= t16;
@@ -575,14 +612,15 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
       const uint32_t pos = wfill + lane_rank(bm);
       if (cand && pos < (uint32_t)kSegV) {
         my_vec[pos] = d[i];
-        my_vi[pos] = (uint32_t)(i * kB + tid);
-        my_vm[pos] = mv;
+        my_vim[pos] = (uint32_t)(i * kB + tid) | ((uint32_t)mv << 16);
       }
       wfill += (uint32_t)__popcll(bm);
     }
-    if (i == NB - 1 && NB < NV) {     // count the first half while the rest streams in
+    // count what is stored so far while the rest streams in: after the first
+    // half, and after three quarters, so little is left for the end
+    if ((i == NB - 1 || i == NB + NB / 2 - 1) && i + 1 < NV) {
       const uint32_t to = wfill < (uint32_t)kSegV ? wfill : (uint32_t)kSegV;
-      count_stored(0, to);
+      count_stored(counted, to);
       counted = to;
     }
   }
@@ -596,19 +634,15 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   }
   __syncthreads();
 
-  // ---- 3. scan the histogram from the row maximum down to t* = max_w t_w
-  uint32_t kmaxu = 0, tstaru = 0;
-#pragma unroll
-  for (int w = 0; w < kWv; ++w) {
-    kmaxu = fs.wmax[w] > kmaxu ? fs.wmax[w] : kmaxu;
-    tstaru = fs.wthr[w] > tstaru ? fs.wthr[w] : tstaru;
-  }
-  const int32_t kmax16 = (int32_t)kmaxu - 0x8000;
-  const int32_t tstar16 = (int32_t)tstaru - 0x8000;
-  const float inv_t = 1.0f / temp;
-  const float m = __fmul_rn(bits_value(kmax16), inv_t);
-  const bool usable = fs.flag == 0 && kmax16 <= kPosInfBits;   // no NaN, no full segment
+  // ---- 3. wave 0 scans the histogram from the row maximum down to t* = max_w t_w
+  float m = 0.0f;                   // row maximum / T (wave 0)
   if (wid == 0) {
+    const uint32_t kmaxu = wave_max_dpp(lane < kWv ? fs.wmax[lane] : 0u);
+    const uint32_t tstaru = wave_max_dpp(lane < kWv ? fs.wthr[lane] : 0u);
+    const int32_t kmax16 = (int32_t)kmaxu - 0x8000;
+    const int32_t tstar16 = (int32_t)tstaru - 0x8000;
+    m = __fmul_rn(bits_value(kmax16), inv_t);
+    const bool usable = fs.flag == 0 && kmax16 <= kPosInfBits;   // no NaN, no full segment
     ScanOut so{false, 0, 0, 0, 0, 0.0f};
     if (usable) so = scan_hist(fs.hist, tstar16, kmax16, inv_t, m, (uint32_t)kq, p_on, pq);
     if (lane == 0) {
@@ -626,110 +660,126 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
     general::general_row<uint16_t, ROUTE, kOutSample>(a, r, sh.g);
     return;
   }
-  ScanOut o{true, fs.tau_bits, fs.need, fs.n_eq, fs.vc_bits, fs.zp};
-  const uint32_t stored_mine = fs.wcount[wid];
+  const int32_t tau = fs.tau_bits;
+  const int32_t vc = fs.vc_bits;
+  const uint32_t need = fs.need;
+  // a wave whose maximum is below the cutoff holds no member of P (and no
+  // member of the tie group at tau <= cutoff): it skips the member passes
+  const int32_t wmax16 = (int32_t)fs.wmax[wid] - 0x8000;
+  const uint32_t stored_mine = wmax16 >= vc ? fs.wcount[wid] : 0u;
 
-  // ---- 4. lowest indices of the boundary tie group, when P reaches into it
-  uint32_t idx_cut = 0xFFFFFFFFu;
-  if (o.vc_bits == o.tau_bits && o.need < o.n_eq) {
+  // ---- 4. when P ends inside the tie group at tau, publish that group
+  const bool tie_cut = vc == tau && need < fs.n_eq;
+  uint32_t nt = 0;
+  if (tie_cut) {
     for (uint32_t e = lane; e < stored_mine; e += kWave) {
-      if (my_vm[e] < o.tau_bits) continue;
+      const uint32_t vim = my_vim[e];
+      if (((int32_t)vim >> 16) < tau) continue;
       const v4u dv = my_vec[e];
-      const uint32_t vi = my_vi[e];
+      const uint32_t vi = vim & 0xFFFFu;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        if (elem_i16(dv, s) == o.tau_bits) {
+        if (elem_i16(dv, s) == tau) {
           const uint32_t slot = atomicAdd(&fs.nties, 1u);
-          if (slot < (uint32_t)kB) fs.ties[slot] = vi * 8 + (uint32_t)s;
+          if (slot < (uint32_t)kMaxTies) fs.ties[slot] = vi * 8 + (uint32_t)s;
         }
       }
     }
     __syncthreads();
-    const uint32_t nt = fs.nties;
-    if (nt > (uint32_t)kB) {
+    nt = fs.nties;
+    if (nt > (uint32_t)kMaxTies) {
       __syncthreads();
       general::general_row<uint16_t, ROUTE, kOutSample>(a, r, sh.g);
       return;
     }
-    if ((uint32_t)tid < nt) {
-      const uint32_t mine = fs.ties[tid];
-      uint32_t rank = 0;
-      for (uint32_t t = 0; t < nt; ++t) rank += fs.ties[t] < mine ? 1u : 0u;
-      if (rank == o.need - 1) fs.idx_cut = mine;
-    }
-    __syncthreads();
-    idx_cut = fs.idx_cut;
   }
 
-  // ---- 5. compact P over all waves (vector maxima first, one atomic per
-  // wave), then Philox noise for P only and a block argmax
+  // ---- 5. members of P (x >= vc; of the tie group at tau only its `need`
+  // lowest indices), compacted over all waves with one atomic per wave
+  const int32_t thr = tie_cut ? tau + 1 : vc;          // x >= thr: member outright
+  const int32_t eqv = tie_cut ? tau : 0x7FFFFFFF;      // x == eqv: member by rank
   constexpr int kChunks = (kSegV + kWave - 1) / kWave;
-  {
-    uint32_t vsel = 0;      // chunks whose vector holds a member of P (bit per chunk)
+  uint32_t masks[kChunks];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int ch = 0; ch < kChunks; ++ch) {
+    masks[ch] = 0;
+    if ((uint32_t)(ch * kWave) >= stored_mine) continue;   // wave-uniform
+    const uint32_t e = (uint32_t)(ch * kWave + lane);
+    const uint32_t vim = e < stored_mine ? my_vim[e] : 0x80000000u;
+    if (((int32_t)vim >> 16) >= vc) {
+      const v4u dv = my_vec[e];
+      uint32_t mk = 0, eq = 0;
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) {
+        const int32_t val = elem_i16(dv, sl);
+        mk |= (val >= thr ? 1u : 0u) << sl;
+        eq |= (val == eqv ? 1u : 0u) << sl;
+      }
+      if (eq) {
+        const uint32_t vi = vim & 0xFFFFu;
+        do {
+          const int sl = __ffs(eq) - 1;
+          eq &= eq - 1;
+          if (tie_rank(fs.ties, nt, vi * 8 + (uint32_t)sl) < need) mk |= 1u << sl;
+        } while (eq);
+      }
+      masks[ch] = mk;
+      cnt += (uint32_t)__popc(mk);
+    }
+  }
+  const uint32_t incl = wave_scan_u32(cnt);
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+  if (total != 0) {
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&fs.np, total);
+    base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+    uint32_t pos = base + incl - cnt;
 #pragma unroll
     for (int ch = 0; ch < kChunks; ++ch) {
+      uint32_t mask = masks[ch];
+      if (!mask) continue;
       const uint32_t e = (uint32_t)(ch * kWave + lane);
-      if (e < stored_mine && my_vm[e] >= o.vc_bits) vsel |= 1u << ch;
-    }
-    uint32_t masks[kChunks];
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int ch = 0; ch < kChunks; ++ch) {
-      masks[ch] = 0;
-      if (__ballot((vsel >> ch) & 1u) == 0) continue;
-      if ((vsel >> ch) & 1u) {
-        const uint32_t e = (uint32_t)(ch * kWave + lane);
-        const v4u dv = my_vec[e];
-        const uint32_t vi = my_vi[e];
-#pragma unroll
-        for (int sl = 0; sl < 8; ++sl) {
-          const int32_t val = elem_i16(dv, sl);
-          const uint32_t j = vi * 8 + (uint32_t)sl;
-          masks[ch] |= (uint32_t)(val >= o.vc_bits && (val > o.tau_bits || j <= idx_cut)) << sl;
+      const v4u dv = my_vec[e];
+      const uint32_t vi = my_vim[e] & 0xFFFFu;
+      do {
+        const int sl = __ffs(mask) - 1;
+        mask &= mask - 1;
+        if (pos < (uint32_t)kMaxK) {
+          fs.pidx[pos] = vi * 8 + (uint32_t)sl;
+          fs.pval[pos] = bits_value(elem_i16(dv, sl));
         }
-        cnt += (uint32_t)__popc(masks[ch]);
-      }
-    }
-    const uint32_t incl = wave_scan_u32(cnt);
-    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
-    if (total != 0) {
-      uint32_t base = 0;
-      if (lane == 0) base = atomicAdd(&fs.np, total);
-      base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-      uint32_t pos = base + incl - cnt;
-#pragma unroll
-      for (int ch = 0; ch < kChunks; ++ch) {
-        uint32_t mask = masks[ch];
-        if (!mask) continue;
-        const uint32_t e = (uint32_t)(ch * kWave + lane);
-        const v4u dv = my_vec[e];
-        const uint32_t vi = my_vi[e];
-        while (mask) {
-          const int sl = __ffs(mask) - 1;
-          mask &= mask - 1;
-          if (pos < (uint32_t)kB) {
-            fs.pidx[pos] = vi * 8 + (uint32_t)sl;
-            fs.pval[pos] = bits_value(elem_i16(dv, sl));
-          }
-          ++pos;
-        }
-      }
+        ++pos;
+      } while (mask);
     }
   }
   __syncthreads();
-  const uint32_t np = fs.np < (uint32_t)kB ? fs.np : (uint32_t)kB;
-  Pick best{-__builtin_inff(), 0x7FFFFFFF, 0.0f};
-  if ((uint32_t)(wid * kWave) < np) {
-    if ((uint32_t)tid < np) {
-      const NoiseStream ns{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
-                           (uint32_t)a.step_offset, (uint32_t)(a.step_offset >> 32)};
-      const uint32_t j = fs.pidx[tid];
-      const float sv = __fmul_rn(fs.pval[tid], inv_t);
-      best = Pick{sv + gumbel_from_word(ns.word(j)), (int32_t)j, sv};
+
+  // ---- 6. Philox noise for P only and the perturbed argmax: one wave when P
+  // fits in it, else one member per thread and a block argmax
+  const uint32_t np = fs.np < (uint32_t)kMaxK ? fs.np : (uint32_t)kMaxK;
+  const NoiseStream ns{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
+                       (uint32_t)a.step_offset, (uint32_t)(a.step_offset >> 32)};
+  if (np <= (uint32_t)kWave) {
+    if (wid != 0) return;
+    Pick p{-__builtin_inff(), 0x7FFFFFFF, 0.0f};
+    if ((uint32_t)lane < np) {
+      const uint32_t j = fs.pidx[lane];
+      const float sv = __fmul_rn(fs.pval[lane], inv_t);
+      p = Pick{sv + gumbel_from_word(ns.word(j)), (int32_t)j, sv};
     }
+    p = wave_pick(p);
+    if (lane == 0) write_result(a, r, p.j, p.s - m - __logf(fs.zp));
+    return;
+  }
+  Pick best{-__builtin_inff(), 0x7FFFFFFF, 0.0f};
+  if ((uint32_t)tid < np) {
+    const uint32_t j = fs.pidx[tid];
+    const float sv = __fmul_rn(fs.pval[tid], inv_t);
+    best = Pick{sv + gumbel_from_word(ns.word(j)), (int32_t)j, sv};
   }
   best = block_pick(best, fs);
-  if (tid == 0) write_result(a, r, best.j, (float)((double)best.s - (double)m - log((double)o.zp)));
+  if (tid == 0) write_result(a, r, best.j, best.s - m - __logf(fs.zp));
 }
 
 template <int NV>
