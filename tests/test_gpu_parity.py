@@ -122,7 +122,7 @@ def test_edge_rows(case, dtype, k, p, t):
 def test_bf16_like_ties_and_misaligned_stride(dtype):
     rng = np.random.default_rng(12)
     rows = np.round(rng.normal(0, 3, size=(6, 3001)) * 4) / 4     # heavy ties
-    for k, p in [(50, 1.0), (700, 0.8), (0, 0.6), (1, 0.9)]:
+    for k, p in [(50, 1.0), (700, 0.8), (0, 0.6), (1, 0.9), (0, 1.0)]:
         wl = _custom(rows, dtype=dtype, k=k, p=p, t=0.9, stride_pad=3)
         print(f"[case] ties k={k} p={p} {dtype}", flush=True)
         _run_custom(wl)
@@ -177,3 +177,32 @@ def test_argument_errors_on_gpu_handle():
         s.sample(x.half(), 4, prm)
     out = s.sample(x, 0, prm)
     assert out.numel() == 0
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("vocab,stride_pad", [(4099, 0), (20011, 5), (32000, 0), (262147, 1)])
+def test_no_filter_rows_split_over_workgroups(dtype, vocab, stride_pad):
+    """No-filter route: each row is spread over many workgroups whose partial
+    argmax / log-sum-exp results are merged by the last one (odd vocab, padded
+    stride, the largest split)."""
+    rng = np.random.default_rng(vocab)
+    n = 5
+    x = rng.normal(0, 3, size=(n, vocab)).astype(np.float32)
+    x[1, rng.integers(0, vocab, 50)] = -np.inf
+    x[2, :] = 0.5                                     # one big tie group
+    wl = _custom(x, dtype=dtype, k=0, p=1.0, t=1.0, stride_pad=stride_pad)
+    wl.temperature = torch.tensor([1.0, 0.7, 1.3, 0.0, 2.0])
+    print(f"[case] split none {dtype} vocab={vocab} pad={stride_pad}", flush=True)
+    dev = {"logits": _device_logits(wl), "gather": None, "req": None,
+           "params": tsa.SamplingParams(wl.temperature.cuda(), wl.seed.cuda(), wl.top_k.cuda(),
+                                        wl.top_p.cuda())}
+    s = tsa.Sampler(wl.vocab, wl.n)
+    ids, lps = parity.gpu_sample(wl, s, dev)
+    parity.compare_samples(ids, lps, parity.oracle_sample(wl)).check()
+    # the per-row counters are back at zero: a second call gives the same result
+    ids2, lps2 = parity.gpu_sample(wl, s, dev)
+    assert np.array_equal(ids, ids2) and np.array_equal(lps, lps2, equal_nan=True)
+    # another step offset: fresh noise, still the oracle's draw
+    wl.step_offset = 1
+    ids3, lps3 = parity.gpu_sample(wl, s, dev)
+    parity.compare_samples(ids3, lps3, parity.oracle_sample(wl)).check()

@@ -10,6 +10,18 @@ enum Route : int { kRouteNone = 0, kRouteTopK = 1, kRouteTopP = 2, kRouteJoint =
 enum OutMode : int { kOutSample = 0, kOutLogProbFull = 1, kOutLogProbAt = 2 };
 enum DType : int { kF32 = 0, kBF16 = 1 };
 
+// Split-row kernels spread a row over at most kMaxSplit workgroups; each leaves
+// one partial result in the handle's workspace.
+constexpr int kMaxSplit = 64;
+struct alignas(16) SplitPartial {
+  uint32_t o;    // order word of the best entry (0: none)
+  int32_t j;     // its index
+  float s;       // its scaled logit
+  float m;       // log-sum-exp of the part: max ...
+  float sum;     // ... and sum of exp(s - max)
+  uint32_t pad[3];
+};
+
 // Everything a row kernel needs; all pointers are device pointers.
 struct RowArgs {
   const void* logits;
@@ -28,12 +40,18 @@ struct RowArgs {
   const int32_t* token_ids;    // log-probs at ids: [n]
   int32_t mass_shift;          // fixed-point scale of probability masses: 2^mass_shift
   int32_t index_bits;          // ceil(log2(vocab)), at least 1
+  uint32_t* split_counter;     // workspace: [max_rows] zeros between calls
+  void* split_partials;        // workspace: [max_rows * kMaxSplit] SplitPartial
 };
 
 // Picks the kernel for a call (fast register-resident kernel where the row
 // shape allows it, else the general multi-pass kernel) and launches it.
 hipError_t launch_rows(const RowArgs& a, DType dtype, Route route, OutMode mode,
                        hipStream_t stream);
+
+// Split-row kernel for calls whose every row is unfiltered (no-filter route).
+bool split_none_supported(const RowArgs& a);
+hipError_t launch_rows_split_none(const RowArgs& a, DType dtype, hipStream_t stream);
 
 // The general multi-pass kernel alone (every row shape).
 hipError_t launch_rows_general(const RowArgs& a, DType dtype, Route route, OutMode mode,

@@ -807,6 +807,9 @@ hipError_t launch_nv(const RowArgs& a, Route route, hipStream_t stream) {
 hipError_t launch_rows(const RowArgs& a, DType dtype, Route route, OutMode mode,
                        hipStream_t stream) {
   if (a.n <= 0) return hipSuccess;
+  // every row unfiltered: noise for every entry, rows split over workgroups
+  if (mode == kOutSample && route == kRouteNone && split_none_supported(a))
+    return launch_rows_split_none(a, dtype, stream);
   const bool aligned = (reinterpret_cast<uintptr_t>(a.logits) % 16) == 0 && (a.row_stride % 8) == 0;
   const int64_t nvec = a.vocab / 8;
   if (dtype == kBF16 && mode == kOutSample && route != kRouteTopP && aligned &&

@@ -15,6 +15,9 @@ struct ts_sampler {
   int32_t device;        // -1: validation-only handle (no GPU work is ever enqueued)
   int32_t index_bits;    // ceil(log2(vocab)), at least 1
   int32_t mass_shift;    // fixed-point scale of masses: sum of vocab masses <= 2^62
+  void* workspace;       // device memory: split-row counters, then partial results
+  uint32_t* split_counter;
+  void* split_partials;
 };
 
 namespace {
@@ -78,6 +81,8 @@ tss::RowArgs make_args(const ts_sampler* s, const void* logits, int64_t row_stri
   a.seed = p->seed;
   a.mass_shift = s->mass_shift;
   a.index_bits = s->index_bits;
+  a.split_counter = s->split_counter;
+  a.split_partials = s->split_partials;
   return a;
 }
 
@@ -120,11 +125,43 @@ ts_status ts_create(int64_t vocab, int32_t max_rows, int32_t device, ts_sampler*
   s->index_bits = ceil_log2(vocab) < 1 ? 1 : ceil_log2(vocab);
   const int shift = 62 - ceil_log2(vocab + 1);
   s->mass_shift = shift > 44 ? 44 : shift;
+  s->workspace = nullptr;
+  s->split_counter = nullptr;
+  s->split_partials = nullptr;
+  if (device >= 0) {
+    // counters, padded to 256 bytes, then the partial results
+    const size_t counter_bytes = ((size_t)max_rows * sizeof(uint32_t) + 255) & ~(size_t)255;
+    const size_t bytes = counter_bytes + (size_t)max_rows * tss::kMaxSplit * sizeof(tss::SplitPartial);
+    DeviceGuard guard(device);
+    if (!guard.ok) {
+      delete s;
+      return TS_E_HIP;
+    }
+    void* ws = nullptr;
+    const hipError_t e = hipMalloc(&ws, bytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      delete s;
+      return e == hipErrorOutOfMemory ? TS_E_NOMEM : TS_E_HIP;
+    }
+    if (hipMemset(ws, 0, counter_bytes) != hipSuccess) {
+      (void)hipFree(ws);
+      delete s;
+      return TS_E_HIP;
+    }
+    s->workspace = ws;
+    s->split_counter = static_cast<uint32_t*>(ws);
+    s->split_partials = static_cast<char*>(ws) + counter_bytes;
+  }
   *out = s;
   return TS_OK;
 }
 
 ts_status ts_destroy(ts_sampler* s) {
+  if (s != nullptr && s->workspace != nullptr) {
+    DeviceGuard guard(s->device);
+    (void)hipFree(s->workspace);
+  }
   delete s;
   return TS_OK;
 }
