@@ -22,6 +22,18 @@ struct alignas(16) SplitPartial {
   uint32_t pad[3];
 };
 
+// Per-row state of the top-p route between its two kernels.
+struct alignas(16) TopPRow {
+  uint32_t mode;   // 0: draw from the entries with order key >= key_c; 1: done
+  uint32_t key_c;  // order key of the cutoff tie group
+  float m2;        // row maximum of x log2(e) / T
+  float zp;        // mass of P: sum over P of exp2(s - m2)
+  int64_t src;     // source row in the logits buffer
+  uint64_t seed;   // the request's seed
+  float scale2;    // log2(e) / T
+  uint32_t pad[3];
+};
+
 // Everything a row kernel needs; all pointers are device pointers.
 struct RowArgs {
   const void* logits;
@@ -42,6 +54,7 @@ struct RowArgs {
   int32_t index_bits;          // ceil(log2(vocab)), at least 1
   uint32_t* split_counter;     // workspace: [max_rows] zeros between calls
   void* split_partials;        // workspace: [max_rows * kMaxSplit] SplitPartial
+  TopPRow* topp_rows;          // workspace: [max_rows]
 };
 
 // Picks the kernel for a call (fast register-resident kernel where the row
@@ -52,6 +65,10 @@ hipError_t launch_rows(const RowArgs& a, DType dtype, Route route, OutMode mode,
 // Split-row kernel for calls whose every row is unfiltered (no-filter route).
 bool split_none_supported(const RowArgs& a);
 hipError_t launch_rows_split_none(const RowArgs& a, DType dtype, hipStream_t stream);
+
+// Top-p route: a cutoff kernel (one workgroup per row) and a split draw kernel.
+bool topp_supported(const RowArgs& a);
+hipError_t launch_rows_topp(const RowArgs& a, DType dtype, hipStream_t stream);
 
 // The general multi-pass kernel alone (every row shape).
 hipError_t launch_rows_general(const RowArgs& a, DType dtype, Route route, OutMode mode,

@@ -810,6 +810,9 @@ hipError_t launch_rows(const RowArgs& a, DType dtype, Route route, OutMode mode,
   // every row unfiltered: noise for every entry, rows split over workgroups
   if (mode == kOutSample && route == kRouteNone && split_none_supported(a))
     return launch_rows_split_none(a, dtype, stream);
+  // every row top-p filtered (or unfiltered): cutoff per row, then a split draw
+  if (mode == kOutSample && route == kRouteTopP && topp_supported(a))
+    return launch_rows_topp(a, dtype, stream);
   const bool aligned = (reinterpret_cast<uintptr_t>(a.logits) % 16) == 0 && (a.row_stride % 8) == 0;
   const int64_t nvec = a.vocab / 8;
   if (dtype == kBF16 && mode == kOutSample && route != kRouteTopP && aligned &&

@@ -18,6 +18,7 @@ struct ts_sampler {
   void* workspace;       // device memory: split-row counters, then partial results
   uint32_t* split_counter;
   void* split_partials;
+  tss::TopPRow* topp_rows;
 };
 
 namespace {
@@ -83,6 +84,7 @@ tss::RowArgs make_args(const ts_sampler* s, const void* logits, int64_t row_stri
   a.index_bits = s->index_bits;
   a.split_counter = s->split_counter;
   a.split_partials = s->split_partials;
+  a.topp_rows = s->topp_rows;
   return a;
 }
 
@@ -128,10 +130,14 @@ ts_status ts_create(int64_t vocab, int32_t max_rows, int32_t device, ts_sampler*
   s->workspace = nullptr;
   s->split_counter = nullptr;
   s->split_partials = nullptr;
+  s->topp_rows = nullptr;
   if (device >= 0) {
-    // counters, padded to 256 bytes, then the partial results
+    // counters, padded to 256 bytes, then the partial results, then the
+    // per-row top-p state
     const size_t counter_bytes = ((size_t)max_rows * sizeof(uint32_t) + 255) & ~(size_t)255;
-    const size_t bytes = counter_bytes + (size_t)max_rows * tss::kMaxSplit * sizeof(tss::SplitPartial);
+    const size_t partial_bytes = (size_t)max_rows * tss::kMaxSplit * sizeof(tss::SplitPartial);
+    const size_t topp_bytes = (size_t)max_rows * sizeof(tss::TopPRow);
+    const size_t bytes = counter_bytes + partial_bytes + topp_bytes;
     DeviceGuard guard(device);
     if (!guard.ok) {
       delete s;
@@ -152,6 +158,7 @@ ts_status ts_create(int64_t vocab, int32_t max_rows, int32_t device, ts_sampler*
     s->workspace = ws;
     s->split_counter = static_cast<uint32_t*>(ws);
     s->split_partials = static_cast<char*>(ws) + counter_bytes;
+    s->topp_rows = reinterpret_cast<tss::TopPRow*>(static_cast<char*>(ws) + counter_bytes + partial_bytes);
   }
   *out = s;
   return TS_OK;
