@@ -78,6 +78,8 @@ struct FastShared {
   uint32_t scan_ok;
   uint32_t nties;
   uint32_t np;
+  uint32_t npc;                    // entries >= the cutoff (when P holds whole groups)
+  uint32_t tmax;                   // largest wave threshold published so far
 };
 
 union RowShared {
@@ -323,6 +325,7 @@ struct ScanOut {
   uint32_t n_eq;      // size of that tie group
   int32_t vc_bits;    // the top-p cutoff value (P = K and x >= cutoff)
   float zp;           // mass of P in units of exp(x_max / T)
+  uint32_t npc;       // entries >= vc_bits (0xFFFFFFFF: not computed)
 };
 
 // Softmax weight exp(x / T - m) of the positive bf16 pattern b.
@@ -340,12 +343,12 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
                                              float inv_t, float m, uint32_t k, bool p_on,
                                              float p) {
   const int lane = threadIdx.x & (kWave - 1);
-  ScanOut o{false, 0, 0, 0, 0, 0.0f};
+  ScanOut o{false, 0, 0, 0, 0, 0.0f, 0xFFFFFFFFu};
   uint32_t cbase = 0, n_gt = 0;
   float mbase = 0.0f, mass_gt = 0.0f;
   bool in_first = true;
-  uint32_t cc[4];
-  float mm[4], mx[4];   // per bin: count, mass, mass of the bins above it
+  uint32_t cc[4], cx[4];
+  float mm[4], mx[4];   // per bin: count, mass; count and mass of the bins above it
   for (int32_t top = hi; top >= lo; top -= 4 * kWave) {
     uint32_t cs = 0;
     float ms = 0.0f;
@@ -369,6 +372,7 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       mx[i] = mex;
+      cx[i] = cex;
       if (cex < k && cex + cc[i] >= k) {   // at most one bin of the row crosses k
         hit = top - (4 * lane + i);
         h_gt = cex;
@@ -397,11 +401,13 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
   const float zk = mass_gt + (float)o.need * bin_weight(o.tau_bits, inv_t, m);
   o.vc_bits = o.tau_bits;
   o.zp = zk;
+  o.npc = k;
   if (!p_on) return o;
   const float target = p * zk;
   if (in_first) {
     int32_t hit = -1;
     float h_z = 0.0f;
+    uint32_t h_n = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int32_t b = hi - (4 * lane + i);
@@ -410,6 +416,7 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
           (mx[i] < target || b == hi)) {
         hit = b;
         h_z = cum;
+        h_n = (b == o.tau_bits) ? k : cx[i] + cc[i];
       }
     }
     const unsigned long long hm = __ballot(hit >= 0);
@@ -417,9 +424,11 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
       const int sl = __ffsll((long long)hm) - 1;
       o.vc_bits = __builtin_amdgcn_readlane(hit, sl);
       o.zp = readlane_f(h_z, sl);
+      o.npc = (uint32_t)__builtin_amdgcn_readlane((int)h_n, sl);
     }
     return o;
   }
+  o.npc = 0xFFFFFFFFu;
   float mb = 0.0f;
   for (int32_t top = hi; top >= o.tau_bits; top -= 4 * kWave) {
     bool ne[4];
@@ -545,6 +554,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
       fs.flag = 0;
       fs.nties = 0;
       fs.np = 0;
+      fs.tmax = 0;
     }
   }
   __syncthreads();
@@ -574,29 +584,22 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   const uint32_t c16 = ((uint32_t)kq + kWv - 1) / kWv + 4;
   const uint32_t c = (uint32_t)kq < c16 ? (uint32_t)kq : c16;
   const uint32_t tw = wave_cth_largest16<NG>(gm, c);
-  const int32_t t16 = (int32_t)tw - 0x8000;
-  const bool wave_ok = t16 > 0;    // the signed order is the value order only above +0
+  const bool wave_ok = (int32_t)tw - 0x8000 > 0;   // the signed order is the value order only above +0
+  // t* = max_w t_w is where the scan stops, so an entry below the largest
+  // threshold published so far can never matter: filter with that one
+  uint32_t teff = tw;
   if (lane == 0) {
     fs.wthr[wid] = tw;
     if (!wave_ok) fs.flag = 1;
+    if (wave_ok) teff = max(tw, atomicMax(&fs.tmax, tw));
   }
+  teff = (uint32_t)__builtin_amdgcn_readfirstlane((int)teff);
+  const int32_t t16 = (int32_t)teff - 0x8000;
 
-  // ---- 2. filter vectors into this wave's segment; count entries >= t16
+  // ---- 2. filter vectors into this wave's segment, then count their entries
   uint32_t wfill = 0;               // wave-uniform number of vectors offered
-  uint32_t counted = 0;             // stored vectors already counted
   v4u* my_vec = fs.cvec[wid];
   uint32_t* my_vim = fs.cvim[wid];
-  auto count_stored = [&](uint32_t from, uint32_t to) {
-    wave_lds_sync();
-    for (uint32_t e = from + lane; e < to; e += kWave) {
-      const v4u dv = my_vec[e];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int32_t val = elem_i16(dv, s);
-        if (val >= t16) hist_add(fs.hist, val);
-      }
-    }
-  };
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     int32_t mv;
@@ -616,17 +619,24 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
       }
       wfill += (uint32_t)__popcll(bm);
     }
-    // count what is stored so far while the rest streams in: after the first
-    // half, and after three quarters, so little is left for the end
-    if ((i == NB - 1 || i == NB + NB / 2 - 1) && i + 1 < NV) {
-      const uint32_t to = wfill < (uint32_t)kSegV ? wfill : (uint32_t)kSegV;
-      count_stored(counted, to);
-      counted = to;
-    }
   }
   if (lane == 0 && wfill > (uint32_t)kSegV) fs.flag = 1;   // a full segment lost vectors
   const uint32_t stored = wfill < (uint32_t)kSegV ? wfill : (uint32_t)kSegV;
-  count_stored(counted, stored);
+  {
+    // entries >= the largest threshold published by now (<= t*) go into the
+    // histogram; stored vectors whose maximum is below it are skipped
+    wave_lds_sync();
+    const int32_t tc = max(t16, (int32_t)fs.tmax - 0x8000);
+    for (uint32_t e = lane; e < stored; e += kWave) {
+      if (((int32_t)my_vim[e] >> 16) < tc) continue;
+      const v4u dv = my_vec[e];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int32_t val = elem_i16(dv, s);
+        if (val >= tc) hist_add(fs.hist, val);
+      }
+    }
+  }
   const uint32_t wmaxu = wave_max_dpp((uint32_t)(vmax + 0x8000));
   if (lane == 0) {
     fs.wcount[wid] = stored;
@@ -643,7 +653,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
     const int32_t tstar16 = (int32_t)tstaru - 0x8000;
     m = __fmul_rn(bits_value(kmax16), inv_t);
     const bool usable = fs.flag == 0 && kmax16 <= kPosInfBits;   // no NaN, no full segment
-    ScanOut so{false, 0, 0, 0, 0, 0.0f};
+    ScanOut so{false, 0, 0, 0, 0, 0.0f, 0xFFFFFFFFu};
     if (usable) so = scan_hist(fs.hist, tstar16, kmax16, inv_t, m, (uint32_t)kq, p_on, pq);
     if (lane == 0) {
       fs.scan_ok = so.ok ? 1u : 0u;
@@ -652,6 +662,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
       fs.need = so.need;
       fs.n_eq = so.n_eq;
       fs.zp = so.zp;
+      fs.npc = so.npc;
     }
   }
   __syncthreads();
@@ -663,120 +674,170 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   const int32_t tau = fs.tau_bits;
   const int32_t vc = fs.vc_bits;
   const uint32_t need = fs.need;
-  // a wave whose maximum is below the cutoff holds no member of P (and no
-  // member of the tie group at tau <= cutoff): it skips the member passes
-  const int32_t wmax16 = (int32_t)fs.wmax[wid] - 0x8000;
-  const uint32_t stored_mine = wmax16 >= vc ? fs.wcount[wid] : 0u;
-
-  // ---- 4. when P ends inside the tie group at tau, publish that group
-  const bool tie_cut = vc == tau && need < fs.n_eq;
-  uint32_t nt = 0;
-  if (tie_cut) {
-    for (uint32_t e = lane; e < stored_mine; e += kWave) {
-      const uint32_t vim = my_vim[e];
-      if (((int32_t)vim >> 16) < tau) continue;
-      const v4u dv = my_vec[e];
-      const uint32_t vi = vim & 0xFFFFu;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        if (elem_i16(dv, s) == tau) {
-          const uint32_t slot = atomicAdd(&fs.nties, 1u);
-          if (slot < (uint32_t)kMaxTies) fs.ties[slot] = vi * 8 + (uint32_t)s;
-        }
-      }
-    }
-    __syncthreads();
-    nt = fs.nties;
-    if (nt > (uint32_t)kMaxTies) {
-      __syncthreads();
-      general::general_row<uint16_t, ROUTE, kOutSample>(a, r, sh.g);
-      return;
-    }
-  }
-
-  // ---- 5. members of P (x >= vc; of the tie group at tau only its `need`
-  // lowest indices), compacted over all waves with one atomic per wave
-  const int32_t thr = tie_cut ? tau + 1 : vc;          // x >= thr: member outright
-  const int32_t eqv = tie_cut ? tau : 0x7FFFFFFF;      // x == eqv: member by rank
-  constexpr int kChunks = (kSegV + kWave - 1) / kWave;
-  uint32_t masks[kChunks];
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int ch = 0; ch < kChunks; ++ch) {
-    masks[ch] = 0;
-    if ((uint32_t)(ch * kWave) >= stored_mine) continue;   // wave-uniform
-    const uint32_t e = (uint32_t)(ch * kWave + lane);
-    const uint32_t vim = e < stored_mine ? my_vim[e] : 0x80000000u;
-    if (((int32_t)vim >> 16) >= vc) {
-      const v4u dv = my_vec[e];
-      uint32_t mk = 0, eq = 0;
-#pragma unroll
-      for (int sl = 0; sl < 8; ++sl) {
-        const int32_t val = elem_i16(dv, sl);
-        mk |= (val >= thr ? 1u : 0u) << sl;
-        eq |= (val == eqv ? 1u : 0u) << sl;
-      }
-      if (eq) {
-        const uint32_t vi = vim & 0xFFFFu;
-        do {
-          const int sl = __ffs(eq) - 1;
-          eq &= eq - 1;
-          if (tie_rank(fs.ties, nt, vi * 8 + (uint32_t)sl) < need) mk |= 1u << sl;
-        } while (eq);
-      }
-      masks[ch] = mk;
-      cnt += (uint32_t)__popc(mk);
-    }
-  }
-  const uint32_t incl = wave_scan_u32(cnt);
-  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
-  if (total != 0) {
-    uint32_t base = 0;
-    if (lane == 0) base = atomicAdd(&fs.np, total);
-    base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-    uint32_t pos = base + incl - cnt;
-#pragma unroll
-    for (int ch = 0; ch < kChunks; ++ch) {
-      uint32_t mask = masks[ch];
-      if (!mask) continue;
-      const uint32_t e = (uint32_t)(ch * kWave + lane);
-      const v4u dv = my_vec[e];
-      const uint32_t vi = my_vim[e] & 0xFFFFu;
-      do {
-        const int sl = __ffs(mask) - 1;
-        mask &= mask - 1;
-        if (pos < (uint32_t)kMaxK) {
-          fs.pidx[pos] = vi * 8 + (uint32_t)sl;
-          fs.pval[pos] = bits_value(elem_i16(dv, sl));
-        }
-        ++pos;
-      } while (mask);
-    }
-  }
-  __syncthreads();
-
-  // ---- 6. Philox noise for P only and the perturbed argmax: one wave when P
-  // fits in it, else one member per thread and a block argmax
-  const uint32_t np = fs.np < (uint32_t)kMaxK ? fs.np : (uint32_t)kMaxK;
   const NoiseStream ns{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
                        (uint32_t)a.step_offset, (uint32_t)(a.step_offset >> 32)};
-  if (np <= (uint32_t)kWave) {
+
+  // ---- 4a. P = {x >= vc} with at most 64 members: wave 0 alone finds them in
+  // every wave's segment, draws their noise and picks; the other waves are done
+  if (!(vc == tau && need < fs.n_eq) && fs.npc <= (uint32_t)kWave) {
     if (wid != 0) return;
+    // the segments as one array of 4-entry quads: quad q is segment q / 56
+    constexpr int kQuadsPerSeg = kSegV / 4;
+    constexpr int kRounds = kWv * kQuadsPerSeg / kWave;
+    static_assert(kSegV % 4 == 0 && (kWv * kQuadsPerSeg) % kWave == 0, "quad layout");
+    const v4u* vim4 = reinterpret_cast<const v4u*>(&fs.cvim[0][0]);
+    const uint32_t wc_lane = fs.wcount[lane & (kWv - 1)];   // lane l < 16: segment l's fill
+    unsigned long long mem = 0;      // bit 4 * round + i: a stored vector holding a member
+#pragma unroll
+    for (int rd = 0; rd < kRounds; ++rd) {
+      const uint32_t qd = (uint32_t)(rd * kWave + lane);
+      const uint32_t w = qd / kQuadsPerSeg;
+      const uint32_t e0 = (qd - w * kQuadsPerSeg) * 4;
+      // a round of 64 quads spans at most two segments
+      const int w0 = rd * kWave / kQuadsPerSeg;   // unrolled: a constant
+      const uint32_t wc = (int)w == w0 ? (uint32_t)__builtin_amdgcn_readlane((int)wc_lane, w0)
+                                       : (uint32_t)__builtin_amdgcn_readlane((int)wc_lane, w0 + 1 < kWv ? w0 + 1 : w0);
+      const v4u vv = vim4[qd];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t vim = i == 0 ? vv.x : i == 1 ? vv.y : i == 2 ? vv.z : vv.w;
+        if (e0 + i < wc && ((int32_t)vim >> 16) >= vc) mem |= 1ull << (rd * 4 + i);
+      }
+    }
+    // list the member vectors (at most 64: each holds a member) in lane order
+    const uint32_t nmine = (uint32_t)__popcll(mem);
+    const uint32_t incl = wave_scan_u32(nmine);
+    const uint32_t nvec_p = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+    uint32_t pos = incl - nmine;
+    while (mem) {
+      const int b = __ffsll((long long)mem) - 1;
+      mem &= mem - 1;
+      const uint32_t qd = (uint32_t)((b >> 2) * kWave + lane);
+      const uint32_t w = qd / kQuadsPerSeg;
+      if (pos < (uint32_t)kWave) fs.pidx[pos] = w * kSegV + (qd - w * kQuadsPerSeg) * 4 + (uint32_t)(b & 3);
+      ++pos;
+    }
+    wave_lds_sync();
+    // one listed vector per lane: its members draw their noise
     Pick p{-__builtin_inff(), 0x7FFFFFFF, 0.0f};
-    if ((uint32_t)lane < np) {
-      const uint32_t j = fs.pidx[lane];
-      const float sv = __fmul_rn(fs.pval[lane], inv_t);
-      p = Pick{sv + gumbel_from_word(ns.word(j)), (int32_t)j, sv};
+    if ((uint32_t)lane < min(nvec_p, (uint32_t)kWave)) {
+      const uint32_t f = fs.pidx[lane];
+      const uint32_t w = f / kSegV;
+      const uint32_t e = f - w * kSegV;
+      const v4u dv = fs.cvec[w][e];
+      const uint32_t vi = fs.cvim[w][e] & 0xFFFFu;
+      uint32_t mk = 0;
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) mk |= (elem_i16(dv, sl) >= vc ? 1u : 0u) << sl;
+      while (mk) {
+        const int sl = __ffs(mk) - 1;
+        mk &= mk - 1;
+        const uint32_t j = vi * 8 + (uint32_t)sl;
+        const float sv = __fmul_rn(bits_value(elem_i16(dv, sl)), inv_t);
+        const float z = sv + gumbel_from_word(ns.word(j));
+        if (z > p.z || (z == p.z && (int32_t)j < p.j)) p = Pick{z, (int32_t)j, sv};
+      }
     }
     p = wave_pick(p);
     if (lane == 0) write_result(a, r, p.j, p.s - m - __logf(fs.zp));
     return;
   }
+  // ---- 4b. every other row.  (i) The stored vectors of all segments, taken as
+  // one array of 16 * kSegV slots three or four per thread: those whose
+  // maximum reaches vc hold members and are listed (one atomic per wave);
+  // when P ends inside the tie group at tau, that group's indices are
+  // published too.  (ii) One listed vector per thread: its members draw
+  // their noise, and a block argmax picks.
+  const bool tie_cut = vc == tau && need < fs.n_eq;
+  uint32_t* mvlist = fs.pidx;                          // listed slots (w * kSegV + e)
+  constexpr int kSlots = kWv * kSegV;
+  constexpr int kListRounds = (kSlots + kB - 1) / kB;
+  const uint32_t wc_lane = fs.wcount[lane & (kWv - 1)];   // lane l < 16: segment l's fill
+  bool listed[kListRounds];
+#pragma unroll
+  for (int rd = 0; rd < kListRounds; ++rd) {
+    const uint32_t f = (uint32_t)(rd * kB + tid);
+    listed[rd] = false;
+    if (f < (uint32_t)kSlots) {
+      const uint32_t w = f / kSegV;
+      // the 64 slots of a wave span at most two segments
+      const int w0 = __builtin_amdgcn_readfirstlane((int)((uint32_t)(rd * kB + wid * kWave) / kSegV));
+      const uint32_t wc = (int)w == w0 ? (uint32_t)__builtin_amdgcn_readlane((int)wc_lane, w0)
+                                       : (uint32_t)__builtin_amdgcn_readlane((int)wc_lane, w0 + 1 < kWv ? w0 + 1 : w0);
+      const uint32_t e = f - w * kSegV;
+      if (e < wc) {
+        const uint32_t vim = fs.cvim[w][e];
+        listed[rd] = ((int32_t)vim >> 16) >= vc;
+        if (listed[rd] && tie_cut) {
+          const v4u dv = fs.cvec[w][e];
+          const uint32_t vi = vim & 0xFFFFu;
+#pragma unroll
+          for (int sl = 0; sl < 8; ++sl) {
+            if (elem_i16(dv, sl) == tau) {
+              const uint32_t slot = atomicAdd(&fs.nties, 1u);
+              if (slot < (uint32_t)kMaxTies) fs.ties[slot] = vi * 8 + (uint32_t)sl;
+            }
+          }
+        }
+      }
+    }
+  }
+  {
+    uint32_t tot = 0;
+#pragma unroll
+    for (int rd = 0; rd < kListRounds; ++rd) tot += (uint32_t)__popcll(__ballot(listed[rd]));
+    if (tot) {
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&fs.np, tot);
+      base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+#pragma unroll
+      for (int rd = 0; rd < kListRounds; ++rd) {
+        const unsigned long long bm = __ballot(listed[rd]);
+        const uint32_t pos = base + lane_rank(bm);
+        if (listed[rd] && pos < (uint32_t)kMaxK) mvlist[pos] = (uint32_t)(rd * kB + tid);
+        base += (uint32_t)__popcll(bm);
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t nmv = fs.np;
+  const uint32_t nt = tie_cut ? fs.nties : 0u;
+  if (nmv > (uint32_t)kMaxK || nt > (uint32_t)kMaxTies) {
+    __syncthreads();
+    general::general_row<uint16_t, ROUTE, kOutSample>(a, r, sh.g);
+    return;
+  }
+  // members: x >= thr outright; x == eqv (the tie group at tau, when P ends
+  // inside it) only for the `need` lowest indices of that group
+  const int32_t thr = tie_cut ? tau + 1 : vc;
+  const int32_t eqv = tie_cut ? tau : 0x7FFFFFFF;
   Pick best{-__builtin_inff(), 0x7FFFFFFF, 0.0f};
-  if ((uint32_t)tid < np) {
-    const uint32_t j = fs.pidx[tid];
-    const float sv = __fmul_rn(fs.pval[tid], inv_t);
-    best = Pick{sv + gumbel_from_word(ns.word(j)), (int32_t)j, sv};
+  if ((uint32_t)tid < nmv) {
+    const uint32_t f = mvlist[tid];
+    const uint32_t w = f / kSegV;
+    const uint32_t e = f - w * kSegV;
+    const v4u dv = fs.cvec[w][e];
+    const uint32_t vi = fs.cvim[w][e] & 0xFFFFu;
+    uint32_t mk = 0, eq = 0;
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) {
+      const int32_t val = elem_i16(dv, sl);
+      mk |= (val >= thr ? 1u : 0u) << sl;
+      eq |= (val == eqv ? 1u : 0u) << sl;
+    }
+    while (eq) {
+      const int sl = __ffs(eq) - 1;
+      eq &= eq - 1;
+      if (tie_rank(fs.ties, nt, vi * 8 + (uint32_t)sl) < need) mk |= 1u << sl;
+    }
+    while (mk) {
+      const int sl = __ffs(mk) - 1;
+      mk &= mk - 1;
+      const uint32_t j = vi * 8 + (uint32_t)sl;
+      const float sv = __fmul_rn(bits_value(elem_i16(dv, sl)), inv_t);
+      const float z = sv + gumbel_from_word(ns.word(j));
+      if (z > best.z || (z == best.z && (int32_t)j < best.j)) best = Pick{z, (int32_t)j, sv};
+    }
   }
   best = block_pick(best, fs);
   if (tid == 0) write_result(a, r, best.j, best.s - m - __logf(fs.zp));
