@@ -600,24 +600,28 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   uint32_t wfill = 0;               // wave-uniform number of vectors offered
   v4u* my_vec = fs.cvec[wid];
   uint32_t* my_vim = fs.cvim[wid];
+  // a wave without a usable threshold sends the row to the general body:
+  // nothing of it is stored or counted
+  if (wave_ok) {
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    int32_t mv;
-    if (i < NB) {
-      mv = vm[i];
-    } else {
-      mv = tid < nvec - i * kB ? vec_max_i16(d[i]) : -32768;
-      vmax = max(vmax, mv);
-    }
-    const bool cand = wave_ok && mv >= t16;
-    const unsigned long long bm = __ballot(cand);
-    if (bm) {
-      const uint32_t pos = wfill + lane_rank(bm);
-      if (cand && pos < (uint32_t)kSegV) {
-        my_vec[pos] = d[i];
-        my_vim[pos] = (uint32_t)(i * kB + tid) | ((uint32_t)mv << 16);
+    for (int i = 0; i < NV; ++i) {
+      int32_t mv;
+      if (i < NB) {
+        mv = vm[i];
+      } else {
+        mv = tid < nvec - i * kB ? vec_max_i16(d[i]) : -32768;
+        vmax = max(vmax, mv);
       }
-      wfill += (uint32_t)__popcll(bm);
+      const bool cand = mv >= t16;
+      const unsigned long long bm = __ballot(cand);
+      if (bm) {
+        const uint32_t pos = wfill + lane_rank(bm);
+        if (cand && pos < (uint32_t)kSegV) {
+          my_vec[pos] = d[i];
+          my_vim[pos] = (uint32_t)(i * kB + tid) | ((uint32_t)mv << 16);
+        }
+        wfill += (uint32_t)__popcll(bm);
+      }
     }
   }
   if (lane == 0 && wfill > (uint32_t)kSegV) fs.flag = 1;   // a full segment lost vectors
@@ -627,13 +631,25 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
     // histogram; stored vectors whose maximum is below it are skipped
     wave_lds_sync();
     const int32_t tc = max(t16, (int32_t)fs.tmax - 0x8000);
+    const i16x2 tc2 = __builtin_bit_cast(i16x2, (uint32_t)tc * 0x10001u);
     for (uint32_t e = lane; e < stored; e += kWave) {
-      if (((int32_t)my_vim[e] >> 16) < tc) continue;
+      const int32_t vmx = (int32_t)my_vim[e] >> 16;
+      if (vmx < tc) continue;
       const v4u dv = my_vec[e];
+      // entries below tc: sign bits of the saturated packed differences
+      uint32_t nlt = 0;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int32_t val = elem_i16(dv, s);
-        if (val >= tc) hist_add(fs.hist, val);
+      for (int w = 0; w < 4; ++w)
+        nlt += (uint32_t)__popc(__builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(
+                                    __builtin_bit_cast(i16x2, word_of(dv, w)), tc2)) & 0x80008000u);
+      if (nlt == 7) {                // the maximum is the only entry >= tc
+        hist_add(fs.hist, vmx);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int32_t val = elem_i16(dv, s);
+          if (val >= tc) hist_add(fs.hist, val);
+        }
       }
     }
   }
