@@ -78,7 +78,6 @@ struct FastShared {
   uint32_t scan_ok;
   uint32_t nties;
   uint32_t np;
-  uint32_t npc;                    // entries >= the cutoff (when P holds whole groups)
   uint32_t tmax;                   // largest wave threshold published so far
 };
 
@@ -325,7 +324,6 @@ struct ScanOut {
   uint32_t n_eq;      // size of that tie group
   int32_t vc_bits;    // the top-p cutoff value (P = K and x >= cutoff)
   float zp;           // mass of P in units of exp(x_max / T)
-  uint32_t npc;       // entries >= vc_bits (0xFFFFFFFF: not computed)
 };
 
 // Softmax weight exp(x / T - m) of the positive bf16 pattern b.
@@ -343,12 +341,12 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
                                              float inv_t, float m, uint32_t k, bool p_on,
                                              float p) {
   const int lane = threadIdx.x & (kWave - 1);
-  ScanOut o{false, 0, 0, 0, 0, 0.0f, 0xFFFFFFFFu};
+  ScanOut o{false, 0, 0, 0, 0, 0.0f};
   uint32_t cbase = 0, n_gt = 0;
   float mbase = 0.0f, mass_gt = 0.0f;
   bool in_first = true;
-  uint32_t cc[4], cx[4];
-  float mm[4], mx[4];   // per bin: count, mass; count and mass of the bins above it
+  uint32_t cc[4];
+  float mm[4], mx[4];   // per bin: count, mass, mass of the bins above it
   for (int32_t top = hi; top >= lo; top -= 4 * kWave) {
     uint32_t cs = 0;
     float ms = 0.0f;
@@ -372,7 +370,6 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       mx[i] = mex;
-      cx[i] = cex;
       if (cex < k && cex + cc[i] >= k) {   // at most one bin of the row crosses k
         hit = top - (4 * lane + i);
         h_gt = cex;
@@ -401,13 +398,11 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
   const float zk = mass_gt + (float)o.need * bin_weight(o.tau_bits, inv_t, m);
   o.vc_bits = o.tau_bits;
   o.zp = zk;
-  o.npc = k;
   if (!p_on) return o;
   const float target = p * zk;
   if (in_first) {
     int32_t hit = -1;
     float h_z = 0.0f;
-    uint32_t h_n = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int32_t b = hi - (4 * lane + i);
@@ -416,7 +411,6 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
           (mx[i] < target || b == hi)) {
         hit = b;
         h_z = cum;
-        h_n = (b == o.tau_bits) ? k : cx[i] + cc[i];
       }
     }
     const unsigned long long hm = __ballot(hit >= 0);
@@ -424,11 +418,9 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
       const int sl = __ffsll((long long)hm) - 1;
       o.vc_bits = __builtin_amdgcn_readlane(hit, sl);
       o.zp = readlane_f(h_z, sl);
-      o.npc = (uint32_t)__builtin_amdgcn_readlane((int)h_n, sl);
     }
     return o;
   }
-  o.npc = 0xFFFFFFFFu;
   float mb = 0.0f;
   for (int32_t top = hi; top >= o.tau_bits; top -= 4 * kWave) {
     bool ne[4];
@@ -669,7 +661,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
     const int32_t tstar16 = (int32_t)tstaru - 0x8000;
     m = __fmul_rn(bits_value(kmax16), inv_t);
     const bool usable = fs.flag == 0 && kmax16 <= kPosInfBits;   // no NaN, no full segment
-    ScanOut so{false, 0, 0, 0, 0, 0.0f, 0xFFFFFFFFu};
+    ScanOut so{false, 0, 0, 0, 0, 0.0f};
     if (usable) so = scan_hist(fs.hist, tstar16, kmax16, inv_t, m, (uint32_t)kq, p_on, pq);
     if (lane == 0) {
       fs.scan_ok = so.ok ? 1u : 0u;
@@ -678,7 +670,6 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
       fs.need = so.need;
       fs.n_eq = so.n_eq;
       fs.zp = so.zp;
-      fs.npc = so.npc;
     }
   }
   __syncthreads();
@@ -693,99 +684,25 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   const NoiseStream ns{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
                        (uint32_t)a.step_offset, (uint32_t)(a.step_offset >> 32)};
 
-  // ---- 4a. P = {x >= vc} with at most 64 members: wave 0 alone finds them in
-  // every wave's segment, draws their noise and picks; the other waves are done
-  if (!(vc == tau && need < fs.n_eq) && fs.npc <= (uint32_t)kWave) {
-    if (wid != 0) return;
-    // the segments as one array of 4-entry quads: quad q is segment q / 56
-    constexpr int kQuadsPerSeg = kSegV / 4;
-    constexpr int kRounds = kWv * kQuadsPerSeg / kWave;
-    static_assert(kSegV % 4 == 0 && (kWv * kQuadsPerSeg) % kWave == 0, "quad layout");
-    const v4u* vim4 = reinterpret_cast<const v4u*>(&fs.cvim[0][0]);
-    const uint32_t wc_lane = fs.wcount[lane & (kWv - 1)];   // lane l < 16: segment l's fill
-    unsigned long long mem = 0;      // bit 4 * round + i: a stored vector holding a member
-#pragma unroll
-    for (int rd = 0; rd < kRounds; ++rd) {
-      const uint32_t qd = (uint32_t)(rd * kWave + lane);
-      const uint32_t w = qd / kQuadsPerSeg;
-      const uint32_t e0 = (qd - w * kQuadsPerSeg) * 4;
-      // a round of 64 quads spans at most two segments
-      const int w0 = rd * kWave / kQuadsPerSeg;   // unrolled: a constant
-      const uint32_t wc = (int)w == w0 ? (uint32_t)__builtin_amdgcn_readlane((int)wc_lane, w0)
-                                       : (uint32_t)__builtin_amdgcn_readlane((int)wc_lane, w0 + 1 < kWv ? w0 + 1 : w0);
-      const v4u vv = vim4[qd];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t vim = i == 0 ? vv.x : i == 1 ? vv.y : i == 2 ? vv.z : vv.w;
-        if (e0 + i < wc && ((int32_t)vim >> 16) >= vc) mem |= 1ull << (rd * 4 + i);
-      }
-    }
-    // list the member vectors (at most 64: each holds a member) in lane order
-    const uint32_t nmine = (uint32_t)__popcll(mem);
-    const uint32_t incl = wave_scan_u32(nmine);
-    const uint32_t nvec_p = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
-    uint32_t pos = incl - nmine;
-    while (mem) {
-      const int b = __ffsll((long long)mem) - 1;
-      mem &= mem - 1;
-      const uint32_t qd = (uint32_t)((b >> 2) * kWave + lane);
-      const uint32_t w = qd / kQuadsPerSeg;
-      if (pos < (uint32_t)kWave) fs.pidx[pos] = w * kSegV + (qd - w * kQuadsPerSeg) * 4 + (uint32_t)(b & 3);
-      ++pos;
-    }
-    wave_lds_sync();
-    // one listed vector per lane: its members draw their noise
-    Pick p{-__builtin_inff(), 0x7FFFFFFF, 0.0f};
-    if ((uint32_t)lane < min(nvec_p, (uint32_t)kWave)) {
-      const uint32_t f = fs.pidx[lane];
-      const uint32_t w = f / kSegV;
-      const uint32_t e = f - w * kSegV;
-      const v4u dv = fs.cvec[w][e];
-      const uint32_t vi = fs.cvim[w][e] & 0xFFFFu;
-      uint32_t mk = 0;
-#pragma unroll
-      for (int sl = 0; sl < 8; ++sl) mk |= (elem_i16(dv, sl) >= vc ? 1u : 0u) << sl;
-      while (mk) {
-        const int sl = __ffs(mk) - 1;
-        mk &= mk - 1;
-        const uint32_t j = vi * 8 + (uint32_t)sl;
-        const float sv = __fmul_rn(bits_value(elem_i16(dv, sl)), inv_t);
-        const float z = sv + gumbel_from_word(ns.word(j));
-        if (z > p.z || (z == p.z && (int32_t)j < p.j)) p = Pick{z, (int32_t)j, sv};
-      }
-    }
-    p = wave_pick(p);
-    if (lane == 0) write_result(a, r, p.j, p.s - m - __logf(fs.zp));
-    return;
-  }
-  // ---- 4b. every other row.  (i) The stored vectors of all segments, taken as
-  // one array of 16 * kSegV slots three or four per thread: those whose
-  // maximum reaches vc hold members and are listed (one atomic per wave);
-  // when P ends inside the tie group at tau, that group's indices are
-  // published too.  (ii) One listed vector per thread: its members draw
-  // their noise, and a block argmax picks.
+  // ---- 4. each wave lists its stored vectors whose maximum reaches vc (they
+  // hold the members of P) with one atomic; when P ends inside the tie group
+  // at tau, that group's indices are published as well
   const bool tie_cut = vc == tau && need < fs.n_eq;
   uint32_t* mvlist = fs.pidx;                          // listed slots (w * kSegV + e)
-  constexpr int kSlots = kWv * kSegV;
-  constexpr int kListRounds = (kSlots + kB - 1) / kB;
-  const uint32_t wc_lane = fs.wcount[lane & (kWv - 1)];   // lane l < 16: segment l's fill
-  bool listed[kListRounds];
+  constexpr int kChunks = (kSegV + kWave - 1) / kWave;
+  const uint32_t stored_mine = (int32_t)fs.wmax[wid] - 0x8000 >= vc ? stored : 0u;
+  {
+    bool listed[kChunks];
+    uint32_t tot = 0;
 #pragma unroll
-  for (int rd = 0; rd < kListRounds; ++rd) {
-    const uint32_t f = (uint32_t)(rd * kB + tid);
-    listed[rd] = false;
-    if (f < (uint32_t)kSlots) {
-      const uint32_t w = f / kSegV;
-      // the 64 slots of a wave span at most two segments
-      const int w0 = __builtin_amdgcn_readfirstlane((int)((uint32_t)(rd * kB + wid * kWave) / kSegV));
-      const uint32_t wc = (int)w == w0 ? (uint32_t)__builtin_amdgcn_readlane((int)wc_lane, w0)
-                                       : (uint32_t)__builtin_amdgcn_readlane((int)wc_lane, w0 + 1 < kWv ? w0 + 1 : w0);
-      const uint32_t e = f - w * kSegV;
-      if (e < wc) {
-        const uint32_t vim = fs.cvim[w][e];
-        listed[rd] = ((int32_t)vim >> 16) >= vc;
-        if (listed[rd] && tie_cut) {
-          const v4u dv = fs.cvec[w][e];
+    for (int ch = 0; ch < kChunks; ++ch) {
+      const uint32_t e = (uint32_t)(ch * kWave + lane);
+      listed[ch] = false;
+      if ((uint32_t)(ch * kWave) < stored_mine) {      // wave-uniform
+        const uint32_t vim = e < stored_mine ? my_vim[e] : 0x80000000u;
+        listed[ch] = ((int32_t)vim >> 16) >= vc;
+        if (listed[ch] && tie_cut) {
+          const v4u dv = my_vec[e];
           const uint32_t vi = vim & 0xFFFFu;
 #pragma unroll
           for (int sl = 0; sl < 8; ++sl) {
@@ -795,22 +712,20 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
             }
           }
         }
+        tot += (uint32_t)__popcll(__ballot(listed[ch]));
       }
     }
-  }
-  {
-    uint32_t tot = 0;
-#pragma unroll
-    for (int rd = 0; rd < kListRounds; ++rd) tot += (uint32_t)__popcll(__ballot(listed[rd]));
     if (tot) {
       uint32_t base = 0;
       if (lane == 0) base = atomicAdd(&fs.np, tot);
       base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
 #pragma unroll
-      for (int rd = 0; rd < kListRounds; ++rd) {
-        const unsigned long long bm = __ballot(listed[rd]);
+      for (int ch = 0; ch < kChunks; ++ch) {
+        if ((uint32_t)(ch * kWave) >= stored_mine) break;
+        const unsigned long long bm = __ballot(listed[ch]);
         const uint32_t pos = base + lane_rank(bm);
-        if (listed[rd] && pos < (uint32_t)kMaxK) mvlist[pos] = (uint32_t)(rd * kB + tid);
+        if (listed[ch] && pos < (uint32_t)kMaxK)
+          mvlist[pos] = (uint32_t)(wid * kSegV + ch * kWave + lane);
         base += (uint32_t)__popcll(bm);
       }
     }
@@ -823,8 +738,13 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
     general::general_row<uint16_t, ROUTE, kOutSample>(a, r, sh.g);
     return;
   }
-  // members: x >= thr outright; x == eqv (the tie group at tau, when P ends
-  // inside it) only for the `need` lowest indices of that group
+
+  // ---- 5. one listed vector per thread: its members (x >= thr outright; of
+  // the tie group at tau, when P ends inside it, the `need` lowest indices)
+  // draw their noise.  At most 64 listed vectors: wave 0 alone, else every
+  // wave and a block argmax.
+  const bool one_wave = nmv <= (uint32_t)kWave;
+  if (one_wave && wid != 0) return;
   const int32_t thr = tie_cut ? tau + 1 : vc;
   const int32_t eqv = tie_cut ? tau : 0x7FFFFFFF;
   Pick best{-__builtin_inff(), 0x7FFFFFFF, 0.0f};
@@ -854,6 +774,11 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
       const float z = sv + gumbel_from_word(ns.word(j));
       if (z > best.z || (z == best.z && (int32_t)j < best.j)) best = Pick{z, (int32_t)j, sv};
     }
+  }
+  if (one_wave) {
+    best = wave_pick(best);
+    if (lane == 0) write_result(a, r, best.j, best.s - m - __logf(fs.zp));
+    return;
   }
   best = block_pick(best, fs);
   if (tid == 0) write_result(a, r, best.j, best.s - m - __logf(fs.zp));
