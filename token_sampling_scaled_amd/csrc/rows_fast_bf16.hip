@@ -501,6 +501,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   const v4u* row = reinterpret_cast<const v4u*>(reinterpret_cast<const uint16_t*>(a.logits) +
                                                 src * a.row_stride);
   const int nvec = (int)(a.vocab >> 3);
+  const int nfull = nvec / kB;       // vector slots every thread of the row holds
   const float temp = a.temperature[q];
   const int32_t kq = kHasK ? a.top_k[q] : 0;
   const float pq = kHasP ? a.top_p[q] : 1.0f;
@@ -556,7 +557,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   int32_t vm[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    vm[i] = tid < nvec - i * kB ? vec_max_i16(d[i]) : -32768;
+    vm[i] = (i < nfull || tid < nvec - i * kB) ? vec_max_i16(d[i]) : -32768;
     vmax = max(vmax, vm[i]);
     if (NB + i < NV) {
       __builtin_amdgcn_sched_barrier(0);
@@ -601,7 +602,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
       if (i < NB) {
         mv = vm[i];
       } else {
-        mv = tid < nvec - i * kB ? vec_max_i16(d[i]) : -32768;
+        mv = (i < nfull || tid < nvec - i * kB) ? vec_max_i16(d[i]) : -32768;
         vmax = max(vmax, mv);
       }
       const bool cand = mv >= t16;
