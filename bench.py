@@ -1,6 +1,6 @@
 """Throughput of one sampling step on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--call sample|log_probs] [--gpus 1]
 
 A step is one ts_sample call over the whole batch (every row: filters, noise,
 draw and the fused log-prob), on synthetic logits already resident in HBM.
@@ -47,11 +47,12 @@ def logits_bytes(wl) -> int:
     return wl.n * wl.vocab * wl.logits.element_size()
 
 
-def algorithmic_bytes(wl) -> int:
+def algorithmic_bytes(wl, call: str = "sample") -> int:
     """HBM bytes one step must move: every selected logit read once, plus per
     row its gather and request indices, the request's parameters (T 4 B, k 4 B,
-    p 4 B, seed 8 B) and the outputs (id 4 B, log-prob 4 B)."""
-    per_row = 4 + 8 + 8
+    p 4 B, seed 8 B) and the outputs: id 4 B and log-prob 4 B for a sample
+    call; the full fp32 row of log-probs (4 B per entry) for a log_probs call."""
+    per_row = 4 + 8 + (8 if call == "sample" else 4 * wl.vocab)
     per_row += 0 if wl.no_top_k else 4
     per_row += 0 if wl.no_top_p else 4
     per_row += 0 if wl.gather_indices is None else 4
@@ -70,7 +71,7 @@ def measured_traffic(workload: str):
     return None
 
 
-def cpu_baseline(wl, budget_s: float):
+def cpu_baseline(wl, budget_s: float, call: str = "sample"):
     """The fp64 oracle, single process, on the leading rows of the same workload."""
     import oracle
     x = wl.logits_f64()
@@ -80,9 +81,13 @@ def cpu_baseline(wl, budget_s: float):
     t0 = time.perf_counter()
     done = 0
     while done < wl.n and time.perf_counter() - t0 < budget_s:
-        oracle.sample(x, wl.n, params, gather_indices=gather, token_to_request_index=req,
-                      step_offset=wl.step_offset, no_top_k=wl.no_top_k, no_top_p=wl.no_top_p,
-                      rows=[done])
+        if call == "sample":
+            oracle.sample(x, wl.n, params, gather_indices=gather, token_to_request_index=req,
+                          step_offset=wl.step_offset, no_top_k=wl.no_top_k, no_top_p=wl.no_top_p,
+                          rows=[done])
+        else:
+            oracle.log_probs(x, wl.n, params, gather_indices=gather, token_to_request_index=req,
+                             no_top_k=wl.no_top_k, no_top_p=wl.no_top_p, rows=[done])
         done += 1
     dt = time.perf_counter() - t0
     return {"value": done / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
@@ -97,6 +102,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="joint_128k", choices=sorted(synth.WORKLOAD_IDS))
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: auto)")
+    ap.add_argument("--call", default="sample", choices=("sample", "log_probs"),
+                    help="time ts_sample (default) or ts_log_probs with full [n, V] rows")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -117,7 +124,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     wl = synth.make(args.workload)
-    nbytes = algorithmic_bytes(wl)
+    nbytes = algorithmic_bytes(wl, args.call)
     buf_bytes = wl.logits.numel() * wl.logits.element_size()
     copies = args.copies or max(2, int(np.ceil(400e6 / buf_bytes)))
     logits = [wl.logits.to(dev) for _ in range(copies)]
@@ -155,6 +162,26 @@ def main():
         st = ts_sample(*cargs)
         if st != tsa.TS_OK:
             raise RuntimeError(f"ts_sample failed with status {st}")
+
+    if args.call == "log_probs":
+        full = torch.empty((wl.n, wl.vocab), dtype=torch.float32, device=dev)
+
+        def step_checked(i):
+            sampler.log_probs(logits[i % copies], params, n=wl.n, no_top_k=wl.no_top_k,
+                              no_top_p=wl.no_top_p, gather_indices=gather,
+                              token_to_request_index=req, output=full)
+
+        lp_args = [[sampler._h, ctypes.c_void_p(lg.data_ptr()), dt_code, lg.shape[0], lg.stride(0),
+                    wl.n, None if gather is None else ctypes.c_void_p(gather.data_ptr()),
+                    None if req is None else ctypes.c_void_p(req.data_ptr()), prm_ref,
+                    int(wl.no_top_k), int(wl.no_top_p), None, ctypes.c_void_p(full.data_ptr()),
+                    stream_ptr] for lg in logits]
+        ts_log_probs = lib.ts_log_probs
+
+        def step(i):
+            st = ts_log_probs(*lp_args[i % copies])
+            if st != tsa.TS_OK:
+                raise RuntimeError(f"ts_log_probs failed with status {st}")
 
     if args.copy_probe_mb:
         a = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
@@ -201,14 +228,16 @@ def main():
         "config": {"workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}",
                    "rows": wl.n, "vocab": wl.vocab, "logits_dtype": str(wl.logits.dtype).split(".")[-1],
                    "route": ["none", "top-k", "top-p", "joint"][tsa.select_route(wl.no_top_k, wl.no_top_p)],
+                   "call": args.call,
                    "input_copies": copies, "logits_bytes_per_step": logits_bytes(wl),
                    "algorithmic_bytes_per_step": nbytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(args.workload),
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(args.workload) if args.call == "sample" else None,
                      "kernel_ms_per_launch": kernel_ms},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, args.call)
     print(json.dumps(out), flush=True)
 
 

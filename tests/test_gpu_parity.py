@@ -66,6 +66,23 @@ def test_sample_parity_full_size_sampled_rows(name):
     assert np.all((ids >= 0) & (ids < wl.vocab))
 
 
+@pytest.mark.parametrize("name", ["topk_128k", "joint_128k"])
+def test_log_probs_full_size_sampled_rows(name):
+    """Full [n, V] log-probs at the benchmark size (register-resident bf16 path),
+    checked on ten rows spread over the batch; then the same at the sampled ids."""
+    wl = synth.make(name)
+    print(f"[case] log_probs full {name} rows={wl.n} vocab={wl.vocab}", flush=True)
+    gpu = parity.gpu_log_probs(wl)
+    rows = sorted(set(np.linspace(0, wl.n - 1, 10).astype(int).tolist()))
+    ref = parity.oracle_log_probs(wl, rows=rows)
+    res = parity.oracle_sample(wl, rows=rows)
+    parity.compare_log_probs(gpu, ref, res, rows=rows).check()
+    ids, lps = parity.gpu_sample(wl)
+    at = parity.gpu_log_probs(wl, token_ids=torch.from_numpy(ids.astype(np.int32)))
+    assert np.allclose(at, lps, atol=1e-5, rtol=0)
+    assert np.allclose(at, gpu[np.arange(wl.n), ids], atol=1e-5, rtol=0)
+
+
 def _custom(rows, dtype=torch.float32, k=0, p=1.0, t=1.0, no_top_k=None, no_top_p=None,
             stride_pad=0):
     x = torch.tensor(np.array(rows, dtype=np.float32)).to(dtype)

@@ -79,6 +79,7 @@ struct FastShared {
   uint32_t nties;
   uint32_t np;
   uint32_t tmax;                   // largest wave threshold published so far
+  float mrow;                      // row maximum / T (scan result)
 };
 
 union RowShared {
@@ -481,7 +482,7 @@ __device__ __forceinline__ uint32_t tie_rank(const uint32_t* ties, uint32_t nt, 
   return rank;
 }
 
-template <int NV, int ROUTE>
+template <int NV, int ROUTE, int MODE>
 __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   constexpr bool kHasK = (ROUTE == kRouteTopK || ROUTE == kRouteJoint);
   constexpr bool kHasP = (ROUTE == kRouteTopP || ROUTE == kRouteJoint);
@@ -511,9 +512,10 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   const bool p_on = kHasP && pq < 1.0f - 1e-6f;
 
   // Rows without top-k draw noise for every entry (VALU-bound: nothing to gain
-  // from register residency), and k above kMaxK: general body.
-  if (!greedy && (!k_on || kq > kMaxK)) {
-    general::general_row<uint16_t, ROUTE, kOutSample>(a, r, sh.g);
+  // from register residency), k above kMaxK, and greedy rows asked for
+  // log-probs: general body.
+  if ((!greedy && (!k_on || kq > kMaxK)) || (greedy && MODE != kOutSample)) {
+    general::general_row<uint16_t, ROUTE, MODE>(a, r, sh.g);
     return;
   }
 
@@ -671,17 +673,82 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
       fs.need = so.need;
       fs.n_eq = so.n_eq;
       fs.zp = so.zp;
+      fs.mrow = m;
     }
   }
   __syncthreads();
   if (fs.scan_ok == 0) {
     __syncthreads();
-    general::general_row<uint16_t, ROUTE, kOutSample>(a, r, sh.g);
+    general::general_row<uint16_t, ROUTE, MODE>(a, r, sh.g);
     return;
   }
   const int32_t tau = fs.tau_bits;
   const int32_t vc = fs.vc_bits;
   const uint32_t need = fs.need;
+
+  if constexpr (MODE != kOutSample) {
+    // ---- log-probs of the processed distribution: lp = x/T - m - ln Z_P on
+    // P, -inf elsewhere, written from the registers (full rows), or at one id
+    const bool tie_cut = vc == tau && need < fs.n_eq;
+    uint32_t nt = 0;
+    if (tie_cut) {
+      // publish the tie group at tau: its `need` lowest indices are in P
+      const uint32_t stored_t = (int32_t)fs.wmax[wid] - 0x8000 >= tau ? stored : 0u;
+      for (uint32_t e = lane; e < stored_t; e += kWave) {
+        const uint32_t vim = my_vim[e];
+        if (((int32_t)vim >> 16) < tau) continue;
+        const v4u dv = my_vec[e];
+        const uint32_t vi = vim & 0xFFFFu;
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+          if (elem_i16(dv, sl) == tau) {
+            const uint32_t slot = atomicAdd(&fs.nties, 1u);
+            if (slot < (uint32_t)kMaxTies) fs.ties[slot] = vi * 8 + (uint32_t)sl;
+          }
+        }
+      }
+      __syncthreads();
+      nt = fs.nties;
+      if (nt > (uint32_t)kMaxTies) {
+        __syncthreads();
+        general::general_row<uint16_t, ROUTE, MODE>(a, r, sh.g);
+        return;
+      }
+    }
+    const float mrow = fs.mrow;
+    const float lzp = __logf(fs.zp);
+    const int32_t thr = tie_cut ? tau + 1 : vc;
+    auto lp_of = [&](int32_t val, uint32_t j) -> float {
+      bool keep = val >= thr;
+      if (tie_cut && val == tau) keep = tie_rank(fs.ties, nt, j) < need;
+      return keep ? __fmul_rn(bits_value(val), inv_t) - mrow - lzp : -__builtin_inff();
+    };
+    if (MODE == kOutLogProbAt) {
+      if (tid == 0) {
+        const int64_t j = a.token_ids[r];
+        float out = -__builtin_inff();
+        if (j >= 0 && j < a.vocab) {
+          const uint16_t raw = reinterpret_cast<const uint16_t*>(a.logits)[src * a.row_stride + j];
+          out = lp_of((int32_t)(int16_t)raw, (uint32_t)j);
+        }
+        a.out_lp[r] = out;
+      }
+      return;
+    }
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    f32x4* out_row = reinterpret_cast<f32x4*>(a.out_lp + (int64_t)r * a.vocab);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int vi = i * kB + tid;
+      if (!(i < nfull || vi < nvec)) continue;
+      float o[8];
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) o[sl] = lp_of(elem_i16(d[i], sl), (uint32_t)(vi * 8 + sl));
+      __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, out_row + 2 * vi);
+      __builtin_nontemporal_store(f32x4{o[4], o[5], o[6], o[7]}, out_row + 2 * vi + 1);
+    }
+    return;
+  }
   const NoiseStream ns{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
                        (uint32_t)a.step_offset, (uint32_t)(a.step_offset >> 32)};
 
@@ -736,7 +803,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   const uint32_t nt = tie_cut ? fs.nties : 0u;
   if (nmv > (uint32_t)kMaxK || nt > (uint32_t)kMaxTies) {
     __syncthreads();
-    general::general_row<uint16_t, ROUTE, kOutSample>(a, r, sh.g);
+    general::general_row<uint16_t, ROUTE, MODE>(a, r, sh.g);
     return;
   }
 
@@ -786,20 +853,34 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
 }
 
 template <int NV>
-hipError_t launch_nv(const RowArgs& a, Route route, hipStream_t stream) {
+hipError_t launch_nv(const RowArgs& a, Route route, OutMode mode, hipStream_t stream) {
   const dim3 grid(a.n), block(kB);
+  if (mode == kOutLogProbFull) {        // top-k and joint routes only
+    if (route == kRouteTopK)
+      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteTopK, kOutLogProbFull>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteJoint, kOutLogProbFull>), grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
+  if (mode == kOutLogProbAt) {
+    if (route == kRouteTopK)
+      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteTopK, kOutLogProbAt>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteJoint, kOutLogProbAt>), grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
   switch (route) {
     case kRouteNone:
-      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteNone>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteNone, kOutSample>), grid, block, 0, stream, a);
       break;
     case kRouteTopK:
-      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteTopK>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteTopK, kOutSample>), grid, block, 0, stream, a);
       break;
     case kRouteTopP:
-      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteTopP>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteTopP, kOutSample>), grid, block, 0, stream, a);
       break;
     default:
-      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteJoint>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteJoint, kOutSample>), grid, block, 0, stream, a);
       break;
   }
   return hipGetLastError();
@@ -818,14 +899,17 @@ hipError_t launch_rows(const RowArgs& a, DType dtype, Route route, OutMode mode,
     return launch_rows_topp(a, dtype, stream);
   const bool aligned = (reinterpret_cast<uintptr_t>(a.logits) % 16) == 0 && (a.row_stride % 8) == 0;
   const int64_t nvec = a.vocab / 8;
-  if (dtype == kBF16 && mode == kOutSample && route != kRouteTopP && aligned &&
-      (a.vocab % 8) == 0 && nvec <= 16 * (int64_t)kB) {
+  // the fast kernel: sampling on every route but top-p only; log-probs where
+  // top-k is on (each row without an active top-k runs the general body)
+  const bool fast_route = mode == kOutSample ? route != kRouteTopP
+                                             : (route == kRouteTopK || route == kRouteJoint);
+  if (dtype == kBF16 && fast_route && aligned && (a.vocab % 8) == 0 && nvec <= 16 * (int64_t)kB) {
     const int64_t per = (nvec + kB - 1) / kB;
-    if (per <= 1) return launch_nv<1>(a, route, stream);
-    if (per <= 2) return launch_nv<2>(a, route, stream);
-    if (per <= 4) return launch_nv<4>(a, route, stream);
-    if (per <= 8) return launch_nv<8>(a, route, stream);
-    return launch_nv<16>(a, route, stream);
+    if (per <= 1) return launch_nv<1>(a, route, mode, stream);
+    if (per <= 2) return launch_nv<2>(a, route, mode, stream);
+    if (per <= 4) return launch_nv<4>(a, route, mode, stream);
+    if (per <= 8) return launch_nv<8>(a, route, mode, stream);
+    return launch_nv<16>(a, route, mode, stream);
   }
   return launch_rows_general(a, dtype, route, mode, stream);
 }
