@@ -135,6 +135,25 @@ def test_edge_rows(case, dtype, k, p, t):
     _run_custom(wl)
 
 
+NOK_ROWS = [
+    [1.0, 3.0, 3.0, 2.0, 3.0, -0.0, 0.0, 3.0] * 2,                       # ties at the top
+    [-np.inf, 1.0, np.nan, 2.0, -np.inf, 0.5, -np.nan, -1.0] * 2,        # NaN of both signs
+    [-np.inf] * 16,                                                      # nothing finite
+    [-1.0, -0.0, -2.0, -0.5] * 4,                                        # the maximum is -0
+    [0.5] + [-20.0] * 15,                                                # flat at T = 100
+]
+
+
+@pytest.mark.parametrize("p,t", [(1.0, 1.0), (0.9, 1.0), (0.99, 100.0), (0.0, 0.7)])
+def test_joint_route_rows_without_top_k(p, t):
+    """bf16 rows on the joint route whose own top-k is off: the register-resident
+    body (unfiltered, or top-p by an exact key histogram); a cutoff below its key
+    window (the flat row at T = 100) takes the general body."""
+    wl = _custom(NOK_ROWS, torch.bfloat16, k=0, p=p, t=t, no_top_k=False, no_top_p=False)
+    print(f"[case] joint route without top-k p={p} t={t}", flush=True)
+    _run_custom(wl)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_bf16_like_ties_and_misaligned_stride(dtype):
     rng = np.random.default_rng(12)

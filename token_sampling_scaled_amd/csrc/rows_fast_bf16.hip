@@ -82,8 +82,21 @@ struct FastShared {
   float mrow;                      // row maximum / T (scan result)
 };
 
+// Rows without an active top-k: an exact histogram of order keys over the
+// window [kmax - 32767, kmax] below the row maximum (one bin per bf16 value).
+constexpr int kNoKBins = 32768;
+struct NoKShared {
+  uint32_t hist[kNoKBins];
+  uint32_t wkey[kWv];
+  float wz[kWv];
+  uint32_t vc_key;                 // the cutoff group's order key
+  float zp;                        // mass of P in units of exp(x_max / T)
+  uint32_t ok;                     // 0: the cutoff lies below the window
+};
+
 union RowShared {
   FastShared f;
+  NoKShared n;
   general::Shared g;
 };
 
@@ -482,6 +495,186 @@ __device__ __forceinline__ uint32_t tie_rank(const uint32_t* ties, uint32_t nt, 
   return rank;
 }
 
+// Order key (16 bits) back to the bf16 value it stands for.
+__device__ __forceinline__ float key_value(uint32_t key) {
+  const uint32_t bits = (key & 0x8000u) ? (key & 0x7FFFu) : (~key & 0xFFFFu);
+  return __uint_as_float(bits << 16);
+}
+
+// A sampled row without an active top-k, whole row in registers (d).  P is
+// every finite entry, or with top-p the tie groups from the top whose mass
+// before them stays below p * Z.  Returns false when the row needs the general
+// body instead (NaN or +inf in the row, or a top-p cutoff below the window of
+// 32768 order keys under the row maximum); the caller then synchronises first.
+template <int NV>
+__device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int nfull, const v4u (&d)[NV],
+                        float inv_t, bool p_on, float pq, uint64_t seed, RowShared& sh) {
+  NoKShared& ns_ = sh.n;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
+  // ---- row maximum of the order keys (NaN patterns sort outside the finite range)
+  uint32_t kmx = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (!(i < nfull || i * kB + tid < nvec)) continue;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t k2 = keys2(word_of(d[i], w));
+      kmx = max(kmx, max(canon_key(k2 & 0xFFFFu), canon_key(k2 >> 16)));
+    }
+  }
+  kmx = wave_max_dpp(kmx);
+  if (lane == 0) ns_.wkey[wid] = kmx;
+  if (p_on) {                        // clear the histogram meanwhile
+    v4u* h4 = reinterpret_cast<v4u*>(ns_.hist);
+#pragma unroll
+    for (int i = 0; i < kNoKBins / 4 / kB; ++i) h4[i * kB + tid] = v4u{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  kmx = wave_max_dpp(lane < kWv ? ns_.wkey[lane] : 0u);
+  if (kmx >= kPosInfKey) return false;            // NaN or +inf: general body
+  if (kmx <= kNegInfKey) {                        // no finite entry
+    if (tid == 0) write_result(a, r, -1, __builtin_nanf(""));
+    return true;
+  }
+  const float m = __fmul_rn(key_value(kmx), inv_t);
+
+  // ---- Z = sum over finite entries of exp(x / T - m)
+  float z = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (!(i < nfull || i * kB + tid < nvec)) continue;
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) {
+      const float x = bits_value(elem_i16(d[i], sl) & 0xFFFF);   // any sign
+      const float e = __expf(__fmaf_rn(x, inv_t, -m));
+      z += (x > -__builtin_inff()) ? e : 0.0f;                   // NaN and -inf drop out
+    }
+  }
+  z = wave_sum(z);
+  if (lane == 0) ns_.wz[wid] = z;
+  __syncthreads();
+  z = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWv; ++w) z += ns_.wz[w];
+
+  uint32_t vc_key = kNegInfKey + 1;               // P: every finite entry
+  float zp = z;
+  if (p_on) {
+    // ---- exact histogram of the entries in the window that can be in P:
+    // the entries with s < m + ln((1 - p) Z / V) weigh less than (1 - p) Z
+    // together, so the cutoff is never below them
+    const uint32_t wlo = kmx > (uint32_t)(kNoKBins - 1) ? kmx - (uint32_t)(kNoKBins - 1) : 1u;
+    const float s_lo = m + __logf(fmaxf(1.0f - pq, 0.0f) * z / (float)a.vocab);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if (!(i < nfull || i * kB + tid < nvec)) continue;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t k2 = keys2(word_of(d[i], w));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t key = canon_key(h ? (k2 >> 16) : (k2 & 0xFFFFu));
+          if (key >= wlo && key > kNegInfKey && __fmul_rn(key_value(key), inv_t) >= s_lo)
+            atomicAdd(&ns_.hist[key - wlo], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    // ---- wave 0 scans the bins from the maximum down: the cutoff group is
+    // the first nonempty one whose cumulative mass reaches p Z (the top group
+    // is always kept)
+    if (wid == 0) {
+      const float target = pq * z;
+      float mbase = 0.0f;
+      uint32_t hit_key = 0;
+      float hit_z = 0.0f;
+      bool found = false;
+      for (int32_t top = (int32_t)kmx; top >= (int32_t)wlo && !found; top -= 4 * kWave) {
+        float mm[4];
+        uint32_t cc[4];
+        float ms = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int32_t b = top - (4 * lane + i);
+          cc[i] = b >= (int32_t)wlo ? ns_.hist[b - (int32_t)wlo] : 0u;
+          mm[i] = cc[i] ? (float)cc[i] * __expf(__fmaf_rn(key_value((uint32_t)b), inv_t, -m)) : 0.0f;
+          ms += mm[i];
+        }
+        const float mi = wave_scan_f32(ms);
+        float mex = mbase + (mi - ms);
+        int32_t hit = -1;
+        float h_z = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int32_t b = top - (4 * lane + i);
+          const float cum = mex + mm[i];
+          if (hit < 0 && cc[i] != 0 && cum >= target && (mex < target || b == (int32_t)kmx)) {
+            hit = b;
+            h_z = cum;
+          }
+          mex += mm[i];
+        }
+        const unsigned long long hm = __ballot(hit >= 0);
+        if (hm) {
+          const int sl = __ffsll((long long)hm) - 1;
+          hit_key = (uint32_t)__builtin_amdgcn_readlane(hit, sl);
+          hit_z = readlane_f(h_z, sl);
+          found = true;
+        }
+        mbase += readlane_f(mi, kWave - 1);
+      }
+      if (lane == 0) {
+        ns_.ok = found ? 1u : 0u;
+        ns_.vc_key = hit_key;
+        ns_.zp = hit_z;
+      }
+    }
+    __syncthreads();
+    if (ns_.ok == 0) return false;
+    vc_key = ns_.vc_key;
+    zp = ns_.zp;
+  }
+
+  // ---- Philox noise for the members of P (key >= vc_key), perturbed argmax
+  const NoiseStream nst{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
+                        (uint32_t)a.step_offset, (uint32_t)(a.step_offset >> 32)};
+  Pick best{-__builtin_inff(), 0x7FFFFFFF, 0.0f};
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int vi = i * kB + tid;
+    if (!(i < nfull || vi < nvec)) continue;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // entries 4h .. 4h + 3 of the vector: one Philox block
+      const uint32_t k2a = keys2(word_of(d[i], 2 * h));
+      const uint32_t k2b = keys2(word_of(d[i], 2 * h + 1));
+      const uint32_t kk[4] = {canon_key(k2a & 0xFFFFu), canon_key(k2a >> 16),
+                              canon_key(k2b & 0xFFFFu), canon_key(k2b >> 16)};
+      bool mem[4];
+      bool any = false;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        mem[e] = kk[e] >= vc_key && kk[e] <= kPosInfKey;
+        any |= mem[e];
+      }
+      if (!any) continue;
+      const Philox4 wds = nst.block((uint32_t)(2 * vi + h));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (!mem[e]) continue;
+        const float sv = __fmul_rn(key_value(kk[e]), inv_t);
+        const float zz = sv + gumbel_from_word(wds.v[e]);
+        if (zz > best.z) best = Pick{zz, vi * 8 + 4 * h + e, sv};   // j rises within a thread
+      }
+    }
+  }
+  best = block_pick(best, sh.f);
+  if (tid == 0) write_result(a, r, best.j, best.s - m - __logf(zp));
+  return true;
+}
+
 template <int NV, int ROUTE, int MODE>
 __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   constexpr bool kHasK = (ROUTE == kRouteTopK || ROUTE == kRouteJoint);
@@ -514,7 +707,8 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   // Rows without top-k draw noise for every entry (VALU-bound: nothing to gain
   // from register residency), k above kMaxK, and greedy rows asked for
   // log-probs: general body.
-  if ((!greedy && (!k_on || kq > kMaxK)) || (greedy && MODE != kOutSample)) {
+  const bool nok = MODE == kOutSample && !greedy && !k_on;   // register-resident, below
+  if ((!greedy && !nok && (!k_on || kq > kMaxK)) || (greedy && MODE != kOutSample)) {
     general::general_row<uint16_t, ROUTE, MODE>(a, r, sh.g);
     return;
   }
@@ -529,13 +723,20 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
     const int vi = i * kB + tid;
     d[i] = __builtin_nontemporal_load(row + (vi < nvec ? vi : nvec - 1));
   }
-  if (greedy) {
+  if (greedy || nok) {
 #pragma unroll
     for (int i = NB; i < NV; ++i) {
       const int vi = i * kB + tid;
       d[i] = __builtin_nontemporal_load(row + (vi < nvec ? vi : nvec - 1));
     }
-    greedy_row<NV>(a, r, nvec, d, fs);
+    if (greedy) {
+      greedy_row<NV>(a, r, nvec, d, fs);
+      return;
+    }
+    if (!nok_row<NV>(a, r, nvec, nfull, d, 1.0f / temp, p_on, pq, seed, sh)) {
+      __syncthreads();
+      general::general_row<uint16_t, ROUTE, MODE>(a, r, sh.g);
+    }
     return;
   }
   const float inv_t = 1.0f / temp;
