@@ -43,7 +43,7 @@ namespace {
 constexpr int kB = 1024;
 constexpr int kWv = kB / kWave;
 constexpr int kMaxK = 1024;
-constexpr int kSegV = 224;                 // candidate vectors per wave
+constexpr int kSegV = 256;                 // candidate vectors per wave
 constexpr int kMaxTies = 1024;             // published members of the boundary tie group
 constexpr int kHistBins = 32768;           // one bin per positive bf16 bit pattern
 constexpr uint32_t kNegInfKey = 0x007Fu;
@@ -680,9 +680,14 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   constexpr bool kHasK = (ROUTE == kRouteTopK || ROUTE == kRouteJoint);
   constexpr bool kHasP = (ROUTE == kRouteTopP || ROUTE == kRouteJoint);
   // threshold input: the first NB vectors, in groups of GV vectors (16 entries)
+  // loads in flight: the first NB vectors, then one more per arriving vector;
+  // the wave threshold comes from the first NQ vectors (a quarter of the row
+  // when NV >= 4), in groups of GV vectors (16 entries)
   constexpr int NB = NV >= 2 ? NV / 2 : 1;
-  constexpr int GV = NB >= 2 ? 2 : 1;
-  constexpr int NG = NB / GV;
+  constexpr int NQ = NV >= 4 ? NV / 4 : NB;
+  constexpr int GV = NQ >= 2 ? 2 : 1;
+  constexpr int NG = NQ / GV;
+  constexpr uint32_t kDiv = 8u * NV / NQ;   // c ~ 2k * (share of the row in the sample)
   __shared__ RowShared sh;
   FastShared& fs = sh.f;
 
@@ -755,11 +760,11 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   }
   __syncthreads();
 
-  // ---- 1. this wave's threshold, from the first half of its data
+  // ---- 1. this wave's threshold, from the first NQ vectors of its data
   int32_t vmax = -32768;           // running maximum bit pattern (signed 16-bit order)
-  int32_t vm[NB];
+  int32_t vm[NQ];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
+  for (int i = 0; i < NQ; ++i) {
     vm[i] = (i < nfull || tid < nvec - i * kB) ? vec_max_i16(d[i]) : -32768;
     vmax = max(vmax, vm[i]);
     if (NB + i < NV) {
@@ -777,8 +782,8 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
     for (int v = 1; v < GV; ++v) mg = max(mg, vm[g * GV + v]);
     gm[g] = (uint32_t)(mg + 0x8000);           // unsigned image of the signed order
   }
-  const uint32_t c16 = ((uint32_t)kq + kWv - 1) / kWv + 4;
-  const uint32_t c = (uint32_t)kq < c16 ? (uint32_t)kq : c16;
+  const uint32_t cq = ((uint32_t)kq + kDiv - 1) / kDiv + 4;
+  const uint32_t c = (uint32_t)kq < cq ? (uint32_t)kq : cq;
   const uint32_t tw = wave_cth_largest16<NG>(gm, c);
   const bool wave_ok = (int32_t)tw - 0x8000 > 0;   // the signed order is the value order only above +0
   // t* = max_w t_w is where the scan stops, so an entry below the largest
@@ -792,32 +797,39 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   teff = (uint32_t)__builtin_amdgcn_readfirstlane((int)teff);
   const int32_t t16 = (int32_t)teff - 0x8000;
 
-  // ---- 2. filter vectors into this wave's segment, then count their entries
+  // ---- 2. filter vectors into this wave's segment as they arrive, then count
+  // their entries
   uint32_t wfill = 0;               // wave-uniform number of vectors offered
   v4u* my_vec = fs.cvec[wid];
   uint32_t* my_vim = fs.cvim[wid];
+  auto offer = [&](int i, int32_t mv) {
+    const bool cand = mv >= t16;
+    const unsigned long long bm = __ballot(cand);
+    if (bm) {
+      const uint32_t pos = wfill + lane_rank(bm);
+      if (cand && pos < (uint32_t)kSegV) {
+        my_vec[pos] = d[i];
+        my_vim[pos] = (uint32_t)(i * kB + tid) | ((uint32_t)mv << 16);
+      }
+      wfill += (uint32_t)__popcll(bm);
+    }
+  };
   // a wave without a usable threshold sends the row to the general body:
   // nothing of it is stored or counted
   if (wave_ok) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      int32_t mv;
-      if (i < NB) {
-        mv = vm[i];
-      } else {
-        mv = (i < nfull || tid < nvec - i * kB) ? vec_max_i16(d[i]) : -32768;
-        vmax = max(vmax, mv);
+    for (int i = 0; i < NQ; ++i) offer(i, vm[i]);
+#pragma unroll
+    for (int i = NQ; i < NV; ++i) {
+      const int32_t mv = (i < nfull || tid < nvec - i * kB) ? vec_max_i16(d[i]) : -32768;
+      vmax = max(vmax, mv);
+      if (i < NB && NB + i < NV) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int vi = (NB + i) * kB + tid;
+        d[NB + i] = __builtin_nontemporal_load(row + (vi < nvec ? vi : nvec - 1));
+        __builtin_amdgcn_sched_barrier(0);
       }
-      const bool cand = mv >= t16;
-      const unsigned long long bm = __ballot(cand);
-      if (bm) {
-        const uint32_t pos = wfill + lane_rank(bm);
-        if (cand && pos < (uint32_t)kSegV) {
-          my_vec[pos] = d[i];
-          my_vim[pos] = (uint32_t)(i * kB + tid) | ((uint32_t)mv << 16);
-        }
-        wfill += (uint32_t)__popcll(bm);
-      }
+      offer(i, mv);
     }
   }
   if (lane == 0 && wfill > (uint32_t)kSegV) fs.flag = 1;   // a full segment lost vectors
