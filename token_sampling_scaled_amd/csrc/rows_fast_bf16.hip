@@ -63,7 +63,6 @@ struct FastShared {
   uint32_t pidx[kMaxK];            // kept set P: indices (each wave a range of its own)
   float pval[kMaxK];               //             logits
   uint32_t ties[kMaxTies];         // indices of the boundary tie group
-  uint32_t wthr[kWv];              // per-wave thresholds (biased signed 16-bit order)
   uint32_t wmax[kWv];              // per-wave maxima (same encoding)
   uint32_t wcount[kWv];
   float wz[kWv];
@@ -79,6 +78,7 @@ struct FastShared {
   uint32_t nties;
   uint32_t np;
   uint32_t tmax;                   // largest wave threshold published so far
+  uint32_t kmax;                   // row maximum (unsigned image of the signed order)
   float mrow;                      // row maximum / T (scan result)
 };
 
@@ -756,6 +756,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
       fs.nties = 0;
       fs.np = 0;
       fs.tmax = 0;
+      fs.kmax = 0;
     }
   }
   __syncthreads();
@@ -790,7 +791,6 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   // threshold published so far can never matter: filter with that one
   uint32_t teff = tw;
   if (lane == 0) {
-    fs.wthr[wid] = tw;
     if (!wave_ok) fs.flag = 1;
     if (wave_ok) teff = max(tw, atomicMax(&fs.tmax, tw));
   }
@@ -865,14 +865,17 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   if (lane == 0) {
     fs.wcount[wid] = stored;
     fs.wmax[wid] = wmaxu;
+    atomicMax(&fs.kmax, wmaxu);
   }
   __syncthreads();
 
   // ---- 3. wave 0 scans the histogram from the row maximum down to t* = max_w t_w
   float m = 0.0f;                   // row maximum / T (wave 0)
   if (wid == 0) {
-    const uint32_t kmaxu = wave_max_dpp(lane < kWv ? fs.wmax[lane] : 0u);
-    const uint32_t tstaru = wave_max_dpp(lane < kWv ? fs.wthr[lane] : 0u);
+    // the row maximum and t* = max_w t_w, published with LDS atomics (a wave
+    // without a usable threshold set the flag, so t* is the maximum of all)
+    const uint32_t kmaxu = fs.kmax;
+    const uint32_t tstaru = fs.tmax;
     const int32_t kmax16 = (int32_t)kmaxu - 0x8000;
     const int32_t tstar16 = (int32_t)tstaru - 0x8000;
     m = __fmul_rn(bits_value(kmax16), inv_t);
