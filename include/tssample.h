@@ -30,8 +30,9 @@
  *         members with a strictly larger logit is below p; p >= 1 - 1e-6 keeps
  *         all of K; the top tie group is always kept
  *   g_j = -ln(-ln u_j), u_j = ((w_j >> 9) + 1/2) * 2^-23, w_j = word (j & 3) of
- *         Philox4x32-10(key = seed[q], counter = (j >> 2, r, step_offset lo,
- *         step_offset hi))  (Salmon et al., SC'11)
+ *         Philox4x32-10(key = seed[q], counter = (j >> 2, r, off lo, off hi))
+ *         with off = step_offset (+ step_offsets[q] when given), mod 2^64
+ *         (Salmon et al., SC'11)
  *   id  = argmax over P of s_j + g_j (smallest j on exact ties)
  *   lp  = s_id - logsumexp over P of s
  * A row whose entries are all -inf/NaN yields id -1 and lp NaN.
@@ -94,6 +95,15 @@ typedef struct ts_params {
   const float* top_p;         /* [num_requests]; p >= 1 - 1e-6: filter off */
   const uint64_t* seed;       /* [num_requests] */
   int32_t num_requests;       /* > 0 */
+  /* [num_requests] or NULL.  Per-request Philox offsets, added (mod 2^64) to
+   * the call's step_offset: the request-indexed offset pool of the TokenSpeed
+   * Triton sampling backend page (`offsets_pool`).  Because the kernels read
+   * them from device memory, a call captured in a HIP graph draws fresh noise
+   * on each replay once the caller advances them between replays (the
+   * "flashinfer_sampling" page explains why a captured sampler with the offset
+   * baked in as a constant replays the same random numbers).  Not read by
+   * ts_log_probs, which draws no noise. */
+  const uint64_t* step_offsets;
 } ts_params;
 
 /* Create a sampler for logits rows of `vocab` entries and up to `max_rows`

@@ -239,17 +239,33 @@ def sample(logits, n: int, params: dict, *, gather_indices=None, token_to_reques
     """One sampling step over n output rows (or the listed subset ``rows``).
 
     ``logits`` is a 2-D array [rows_in_buffer, V]; ``params`` maps
-    temperature / top_k / top_p / seed to per-request arrays.  ``no_top_k`` and
-    ``no_top_p`` are the batch-level promises of "flashinfer_sampling"
-    ``sample_kernel``: when set, that filter is off for every row.
+    temperature / top_k / top_p / seed (and optionally step_offsets, a
+    per-request offset pool added to ``step_offset``) to per-request arrays.
+    ``no_top_k`` and ``no_top_p`` are the batch-level promises of
+    "flashinfer_sampling" ``sample_kernel``: when set, that filter is off for
+    every row.
     """
     logits = np.asarray(logits)
+    offsets = params.get("step_offsets")
     out = []
     for r in (range(n) if rows is None else rows):
         src = int(gather_indices[r]) if gather_indices is not None else r
         rp = _row_params(r, params, token_to_request_index)
-        out.append(sample_row(logits[src], rp, r, step_offset, not no_top_k, not no_top_p))
+        out.append(sample_row(logits[src], rp, r, _row_offset(r, step_offset, offsets,
+                                                               token_to_request_index),
+                              not no_top_k, not no_top_p))
     return out
+
+
+def _row_offset(r, step_offset, offsets, token_to_request_index) -> int:
+    """Philox offset of output row r: the call's offset plus, when given, its
+    request's entry of a per-request offset pool, modulo 2^64 (the TokenSpeed
+    Triton sampling backend page passes such a pool, ``offsets_pool``, to every
+    Gumbel kernel)."""
+    if offsets is None:
+        return int(step_offset) % (1 << 64)
+    q = int(token_to_request_index[r]) if token_to_request_index is not None else r
+    return (int(step_offset) + (int(offsets[q]) % (1 << 64))) % (1 << 64)
 
 
 def log_probs(logits, n: int, params: dict, *, gather_indices=None, token_to_request_index=None,

@@ -69,6 +69,7 @@ class Workload:
     no_top_k: bool = False
     no_top_p: bool = False
     step_offset: int = 0
+    step_offsets: Optional[torch.Tensor] = None              # i64 [Q], read as u64
 
     @property
     def vocab(self) -> int:
@@ -80,6 +81,8 @@ class Workload:
             "top_k": self.top_k.numpy().astype(np.int64),
             "top_p": self.top_p.numpy().astype(np.float64),
             "seed": self.seed.numpy().astype(np.int64).view(np.uint64),
+            "step_offsets": None if self.step_offsets is None
+            else self.step_offsets.numpy().astype(np.int64).view(np.uint64),
         }
 
     def logits_f64(self) -> np.ndarray:

@@ -20,7 +20,8 @@ def to_device(wl, device="cuda"):
         "logits": wl.logits.to(device),
         "params": tsa.SamplingParams(
             temperature=wl.temperature.to(device), seed=wl.seed.to(device),
-            top_k=wl.top_k.to(device), top_p=wl.top_p.to(device)),
+            top_k=wl.top_k.to(device), top_p=wl.top_p.to(device),
+            step_offsets=None if wl.step_offsets is None else wl.step_offsets.to(device)),
         "gather": None if wl.gather_indices is None else wl.gather_indices.to(device),
         "req": None if wl.token_to_request_index is None else wl.token_to_request_index.to(device),
     }

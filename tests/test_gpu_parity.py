@@ -83,6 +83,67 @@ def test_log_probs_full_size_sampled_rows(name):
     assert np.allclose(at, gpu[np.arange(wl.n), ids], atol=1e-5, rtol=0)
 
 
+@pytest.mark.parametrize("name,rows,vocab", SMALL)
+def test_per_request_step_offsets(name, rows, vocab):
+    """Per-request offsets read on the device, added to the call's offset."""
+    wl = synth.make(name, rows=rows, vocab=vocab)
+    q = wl.temperature.numel()
+    wl.step_offsets = torch.from_numpy(
+        np.random.default_rng(31).integers(0, 2**63 - 1, q, dtype=np.int64))
+    wl.step_offset = 5
+    print(f"[case] step_offsets {name} rows={wl.n} vocab={wl.vocab}", flush=True)
+    ids, lps = parity.gpu_sample(wl)
+    parity.compare_samples(ids, lps, parity.oracle_sample(wl)).check()
+
+
+@pytest.mark.parametrize("name,rows,vocab", [("joint_128k", 16, 20000), ("topp_152k", 8, 30000),
+                                             ("none_32k", 16, 32000), ("spec_mix", 24, 16384)])
+def test_graph_replay_with_device_offsets(name, rows, vocab):
+    """One call captured in a graph, replayed four times; between replays the
+    per-request offsets advance on the device.  Every replay must equal an eager
+    call at the same offsets (bitwise) and the oracle, and the replays must not
+    all draw the same ids."""
+    wl = synth.make(name, rows=rows, vocab=vocab)
+    q = wl.temperature.numel()
+    dev = parity.to_device(wl)
+    offs = torch.zeros(q, dtype=torch.int64, device="cuda")
+    dev["params"].step_offsets = offs
+    s = tsa.Sampler(wl.vocab, wl.n)
+    ids = torch.empty(wl.n, dtype=torch.int32, device="cuda")
+    lps = torch.empty(wl.n, dtype=torch.float32, device="cuda")
+
+    def call():
+        s.sample(dev["logits"], wl.n, dev["params"], no_top_k=wl.no_top_k, no_top_p=wl.no_top_p,
+                 gather_indices=dev["gather"], token_to_request_index=dev["req"],
+                 step_offset=wl.step_offset, output=ids, logprob_output=lps)
+
+    print(f"[case] graph {name} rows={wl.n} vocab={wl.vocab}", flush=True)
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    check_rows = sorted(set(np.linspace(0, wl.n - 1, 6).astype(int).tolist()))
+    seen = set()
+    for step in range(4):
+        offs.fill_(7 * step + 1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_ids, got_lps = ids.cpu().numpy().copy(), lps.cpu().numpy().copy()
+        call()
+        torch.cuda.synchronize()
+        assert np.array_equal(got_ids, ids.cpu().numpy())
+        assert np.array_equal(got_lps.view(np.int32), lps.cpu().numpy().view(np.int32))
+        wl.step_offsets = offs.cpu()
+        rep = parity.compare_samples(got_ids, got_lps, parity.oracle_sample(wl, rows=check_rows),
+                                     rows=check_rows)
+        rep.check()
+        seen.add(tuple(got_ids.tolist()))
+    assert len(seen) > 1
+
+
 def _custom(rows, dtype=torch.float32, k=0, p=1.0, t=1.0, no_top_k=None, no_top_p=None,
             stride_pad=0):
     x = torch.tensor(np.array(rows, dtype=np.float32)).to(dtype)

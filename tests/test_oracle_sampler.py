@@ -214,6 +214,30 @@ def test_step_offset_and_seed_reproducibility():
     assert len(set(a)) > 10
 
 
+def test_per_request_offsets_add_to_the_call_offset():
+    """A row sampled with a per-request offset pool draws the noise of a plain
+    call made at (step_offset + pool[q]) mod 2^64, q being the row's request."""
+    rng = np.random.default_rng(12)
+    logits = rng.normal(0, 2, size=(10, 48))
+    params = {"temperature": np.full(4, 0.9), "top_k": np.array([0, 7, 0, 12]),
+              "top_p": np.array([1.0, 1.0, 0.8, 0.6]),
+              "seed": np.array([5, 6, 7, 8], dtype=np.uint64),
+              "step_offsets": np.array([0, 3, 2**64 - 1, 2**40], dtype=np.uint64)}
+    req = np.array([0, 1, 2, 3, 0, 1, 2, 3, 1, 2])
+    base = 2**64 - 2
+    got = oracle.sample(logits, 10, params, token_to_request_index=req, step_offset=base)
+    plain = {k: v for k, v in params.items() if k != "step_offsets"}
+    for r in range(10):
+        off = (base + int(params["step_offsets"][req[r]])) % 2**64
+        want = oracle.sample(logits, 10, plain, token_to_request_index=req, step_offset=off,
+                             rows=[r])[0]
+        assert got[r].token == want.token and got[r].logprob == want.logprob
+    # the pool reaches the noise: over many pools the unfiltered row changes its draw
+    draws = {oracle.sample(logits, 10, dict(plain, step_offsets=np.full(4, o, dtype=np.uint64)),
+                           token_to_request_index=req, rows=[0])[0].token for o in range(40)}
+    assert len(draws) > 5
+
+
 def test_near_tie_is_flagged_with_both_alternatives():
     j = np.arange(6)
     g = philox.gumbel_from_uniform(philox.uniform_from_words(philox.noise_words(3, 0, 0, j)))

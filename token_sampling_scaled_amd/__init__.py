@@ -41,7 +41,7 @@ _STATUS_ERRORS = {TS_E_ARG: ValueError, TS_E_DTYPE: TypeError, TS_E_SIZE: ValueE
 class _Params(ctypes.Structure):
     _fields_ = [("temperature", ctypes.c_void_p), ("top_k", ctypes.c_void_p),
                 ("top_p", ctypes.c_void_p), ("seed", ctypes.c_void_p),
-                ("num_requests", ctypes.c_int32)]
+                ("num_requests", ctypes.c_int32), ("step_offsets", ctypes.c_void_p)]
 
 
 _lib = None
@@ -109,20 +109,24 @@ class SamplingParams:
     seed: torch.Tensor                   # int64 [Q] (read as uint64)
     top_k: Optional[torch.Tensor] = None  # int32 [Q]; k <= 0 or k >= V: off
     top_p: Optional[torch.Tensor] = None  # float32 [Q]; p >= 1 - 1e-6: off
+    # int64 [Q] (read as uint64): per-request Philox offsets added to the call's
+    # step_offset; read on the device, so a captured call can be advanced
+    step_offsets: Optional[torch.Tensor] = None
 
     def _struct(self, device) -> _Params:
         q = self.temperature.numel()
         for name, t, dt in (("temperature", self.temperature, torch.float32),
                             ("seed", self.seed, torch.int64),
                             ("top_k", self.top_k, torch.int32),
-                            ("top_p", self.top_p, torch.float32)):
+                            ("top_p", self.top_p, torch.float32),
+                            ("step_offsets", self.step_offsets, torch.int64)):
             if t is None:
                 continue
             if t.dtype != dt or t.device != device or not t.is_contiguous() or t.numel() != q:
                 raise ValueError(f"params.{name} must be a contiguous {dt} tensor of {q} "
                                  f"entries on {device}")
         return _Params(_ptr(self.temperature), _ptr(self.top_k), _ptr(self.top_p),
-                       _ptr(self.seed), q)
+                       _ptr(self.seed), q, _ptr(self.step_offsets))
 
 
 def select_route(no_top_k: bool, no_top_p: bool) -> int:

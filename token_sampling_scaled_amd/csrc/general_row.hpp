@@ -360,8 +360,9 @@ __device__ __forceinline__ void general_row(const RowArgs& a, int r, Shared& sh)
 
   // ---- F: mass of P, then noise + argmax (sample) or the log-prob write.
   if (MODE == kOutSample) {
+    const uint64_t off = noise_offset(a, q);
     const NoiseStream ns{(uint32_t)a.seed[q], (uint32_t)(a.seed[q] >> 32), (uint32_t)r,
-                         (uint32_t)a.step_offset, (uint32_t)(a.step_offset >> 32)};
+                         (uint32_t)off, (uint32_t)(off >> 32)};
     ArgBest best{-__builtin_inff(), 0x7FFFFFFF};
     unsigned long long zp = 0;
     for_groups(row, v, vec, [&](int64_t j0, const uint32_t* raw) {

@@ -31,7 +31,8 @@ struct alignas(16) TopPRow {
   int64_t src;     // source row in the logits buffer
   uint64_t seed;   // the request's seed
   float scale2;    // log2(e) / T
-  uint32_t pad[3];
+  uint32_t pad;
+  uint64_t off;    // the request's Philox offset in this call
 };
 
 // Everything a row kernel needs; all pointers are device pointers.
@@ -47,6 +48,7 @@ struct RowArgs {
   const float* top_p;          // [Q] (null on routes without top-p)
   const uint64_t* seed;        // [Q]
   uint64_t step_offset;
+  const uint64_t* req_offset;  // [Q] or null: per-request offsets added to step_offset
   int32_t* out_ids;            // sample: [n]
   float* out_lp;               // sample: [n] or null; log-probs: [n, vocab] or [n]
   const int32_t* token_ids;    // log-probs at ids: [n]
@@ -56,6 +58,11 @@ struct RowArgs {
   void* split_partials;        // workspace: [max_rows * kMaxSplit] SplitPartial
   TopPRow* topp_rows;          // workspace: [max_rows]
 };
+
+// Philox offset of request q in this call.
+__device__ __forceinline__ uint64_t noise_offset(const RowArgs& a, int64_t q) {
+  return a.step_offset + (a.req_offset ? a.req_offset[q] : 0ull);
+}
 
 // Picks the kernel for a call (fast register-resident kernel where the row
 // shape allows it, else the general multi-pass kernel) and launches it.

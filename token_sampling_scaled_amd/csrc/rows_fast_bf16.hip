@@ -508,7 +508,8 @@ __device__ __forceinline__ float key_value(uint32_t key) {
 // 32768 order keys under the row maximum); the caller then synchronises first.
 template <int NV>
 __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int nfull, const v4u (&d)[NV],
-                        float inv_t, bool p_on, float pq, uint64_t seed, RowShared& sh) {
+                        float inv_t, bool p_on, float pq, uint64_t seed, uint64_t off,
+                        RowShared& sh) {
   NoKShared& ns_ = sh.n;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -639,7 +640,7 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
 
   // ---- Philox noise for the members of P (key >= vc_key), perturbed argmax
   const NoiseStream nst{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
-                        (uint32_t)a.step_offset, (uint32_t)(a.step_offset >> 32)};
+                        (uint32_t)off, (uint32_t)(off >> 32)};
   Pick best{-__builtin_inff(), 0x7FFFFFFF, 0.0f};
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -738,7 +739,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
       greedy_row<NV>(a, r, nvec, d, fs);
       return;
     }
-    if (!nok_row<NV>(a, r, nvec, nfull, d, 1.0f / temp, p_on, pq, seed, sh)) {
+    if (!nok_row<NV>(a, r, nvec, nfull, d, 1.0f / temp, p_on, pq, seed, noise_offset(a, q), sh)) {
       __syncthreads();
       general::general_row<uint16_t, ROUTE, MODE>(a, r, sh.g);
     }
@@ -965,8 +966,9 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
     }
     return;
   }
+  const uint64_t off = noise_offset(a, q);
   const NoiseStream ns{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
-                       (uint32_t)a.step_offset, (uint32_t)(a.step_offset >> 32)};
+                       (uint32_t)off, (uint32_t)(off >> 32)};
 
   // ---- 4. each wave lists its stored vectors whose maximum reaches vc (they
   // hold the members of P) with one atomic; when P ends inside the tie group

@@ -109,8 +109,9 @@ __global__ __launch_bounds__(kSplitBlock) void rows_split_none_kernel(RowArgs a,
         mloc = fmaxf(mloc, sv[i][e]);
       }
     }
+    const uint64_t off = noise_offset(a, q);
     const NoiseStream ns{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
-                         (uint32_t)a.step_offset, (uint32_t)(a.step_offset >> 32)};
+                         (uint32_t)off, (uint32_t)(off >> 32)};
     float sum = 0.0f;
     float bz = -__builtin_inff();
     int32_t bj = 0x7FFFFFFF;

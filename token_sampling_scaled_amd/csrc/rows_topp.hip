@@ -292,6 +292,7 @@ __global__ __launch_bounds__(kCutBlock) void rows_topp_cutoff_kernel(RowArgs a) 
       st->src = src;
       st->seed = a.seed[q];
       st->scale2 = scale2;
+      st->off = noise_offset(a, q);
     }
     return;
   }
@@ -388,6 +389,7 @@ __global__ __launch_bounds__(kCutBlock) void rows_topp_cutoff_kernel(RowArgs a) 
     st->src = src;
     st->seed = a.seed[q];
     st->scale2 = scale2;
+    st->off = noise_offset(a, q);
   }
 }
 
@@ -424,8 +426,9 @@ __global__ __launch_bounds__(kSplitBlock) void rows_topp_draw_kernel(RowArgs a, 
     const T* row = reinterpret_cast<const T*>(a.logits) + st->src * a.row_stride;
     const float scale2 = st->scale2;
     const uint64_t seed = st->seed;
+    const uint64_t off = st->off;
     const NoiseStream ns{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
-                         (uint32_t)a.step_offset, (uint32_t)(a.step_offset >> 32)};
+                         (uint32_t)off, (uint32_t)(off >> 32)};
     const int32_t t0 = tile * kTile;
     const int32_t t_end = t0 + kTile < groups ? t0 + kTile : groups;
 

@@ -189,6 +189,7 @@ ts_status ts_sample(ts_sampler* s, const void* logits, ts_dtype dtype, int64_t r
   tss::RowArgs a = make_args(s, logits, row_stride, n, gather_indices, token_to_request_index,
                              params, no_top_k, no_top_p);
   a.step_offset = step_offset;
+  a.req_offset = params->step_offsets;
   a.out_ids = out_ids;
   a.out_lp = out_logprob;
   const tss::Route route = (tss::Route)ts_select_route(no_top_k, no_top_p);
