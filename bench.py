@@ -51,7 +51,12 @@ def algorithmic_bytes(wl, call: str = "sample") -> int:
     """HBM bytes one step must move: every selected logit read once, plus per
     row its gather and request indices, the request's parameters (T 4 B, k 4 B,
     p 4 B, seed 8 B) and the outputs: id 4 B and log-prob 4 B for a sample
-    call; the full fp32 row of log-probs (4 B per entry) for a log_probs call."""
+    call; the full fp32 row of log-probs (4 B per entry) for a log_probs call.
+    A raw_log_probs call reads only the logits, the gather index and the token
+    id (4 B) and writes one fp32 per row."""
+    if call == "raw_log_probs":
+        per_row = 4 + 4 + (0 if wl.gather_indices is None else 4)
+        return logits_bytes(wl) + wl.n * per_row
     per_row = 4 + 8 + (8 if call == "sample" else 4 * wl.vocab)
     per_row += 0 if wl.no_top_k else 4
     per_row += 0 if wl.no_top_p else 4
@@ -85,6 +90,9 @@ def cpu_baseline(wl, budget_s: float, call: str = "sample"):
             oracle.sample(x, wl.n, params, gather_indices=gather, token_to_request_index=req,
                           step_offset=wl.step_offset, no_top_k=wl.no_top_k, no_top_p=wl.no_top_p,
                           rows=[done])
+        elif call == "raw_log_probs":
+            oracle.raw_log_probs_at(x, wl.n, np.zeros(wl.n, dtype=np.int32),
+                                    gather_indices=gather, rows=[done])
         else:
             oracle.log_probs(x, wl.n, params, gather_indices=gather, token_to_request_index=req,
                              no_top_k=wl.no_top_k, no_top_p=wl.no_top_p, rows=[done])
@@ -102,8 +110,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="joint_128k", choices=sorted(synth.WORKLOAD_IDS))
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: auto)")
-    ap.add_argument("--call", default="sample", choices=("sample", "log_probs"),
-                    help="time ts_sample (default) or ts_log_probs with full [n, V] rows")
+    ap.add_argument("--call", default="sample", choices=("sample", "log_probs", "raw_log_probs"),
+                    help="time ts_sample (default), ts_log_probs with full [n, V] rows, or "
+                         "ts_raw_log_probs_at at the sampled ids")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -182,6 +191,27 @@ def main():
             st = ts_log_probs(*lp_args[i % copies])
             if st != tsa.TS_OK:
                 raise RuntimeError(f"ts_log_probs failed with status {st}")
+
+    if args.call == "raw_log_probs":
+        step_checked(0)                    # the ids to read: one sample of the workload
+        torch.cuda.synchronize()
+        tok = ids.clone()
+        raw = torch.empty(wl.n, dtype=torch.float32, device=dev)
+
+        def step_checked(i):
+            sampler.raw_log_probs_at(logits[i % copies], tok, n=wl.n, gather_indices=gather,
+                                     output=raw)
+
+        raw_args = [[sampler._h, ctypes.c_void_p(lg.data_ptr()), dt_code, lg.shape[0], lg.stride(0),
+                     wl.n, None if gather is None else ctypes.c_void_p(gather.data_ptr()),
+                     ctypes.c_void_p(tok.data_ptr()), ctypes.c_void_p(raw.data_ptr()), stream_ptr]
+                    for lg in logits]
+        ts_raw = lib.ts_raw_log_probs_at
+
+        def step(i):
+            st = ts_raw(*raw_args[i % copies])
+            if st != tsa.TS_OK:
+                raise RuntimeError(f"ts_raw_log_probs_at failed with status {st}")
 
     if args.copy_probe_mb:
         a = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device=dev)

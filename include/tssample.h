@@ -157,6 +157,24 @@ ts_status ts_log_probs(ts_sampler* sampler, const void* logits, ts_dtype dtype,
                        const ts_params* params, int32_t no_top_k, int32_t no_top_p,
                        const int32_t* token_ids, float* out, void* stream);
 
+/* Log-probs of the raw logits at given ids: for every output row r,
+ *   out[r] = x[src, id] - logsumexp_j x[src, j]  over the whole row,
+ * with no temperature and no filter (the selected-token log-probs that the
+ * TokenSpeed Triton sampling backend page writes from the logits and the
+ * sampled ids).  NaN logits read as -inf; a NaN or -inf entry at id gives
+ * -inf; an id outside [0, vocab) or a row with no finite logit gives NaN.
+ *   logits, dtype, rows_in_buffer, row_stride, n, gather_indices  as for ts_sample
+ *   token_ids   device int32 [n]
+ *   out         device float [n], written
+ *   stream      hipStream_t
+ * Uses the handle's workspace (one call per handle at a time).
+ * Errors: TS_E_ARG, TS_E_DTYPE, TS_E_SIZE (host-side checks, or a vocabulary
+ * too large for the split kernel: more than 64 * 16384 entries), TS_E_HIP. */
+ts_status ts_raw_log_probs_at(ts_sampler* sampler, const void* logits, ts_dtype dtype,
+                              int64_t rows_in_buffer, int64_t row_stride, int32_t n,
+                              const int32_t* gather_indices, const int32_t* token_ids,
+                              float* out, void* stream);
+
 /* Per-row request index of the speculative-verify layout
  * ("core.inference.sampling.base", sample_speculative): decode request d in
  * [0, num_decode) owns rows d*(1+num_spec) .. d*(1+num_spec)+num_spec, prefill

@@ -39,6 +39,7 @@ from .sampler import (
     process_row,
     sample_row,
     sample,
+    raw_log_probs_at,
     log_probs,
     build_spec_map,
     GREEDY_T_MAX,
@@ -49,6 +50,6 @@ from .sampler import (
 __all__ = [
     "philox4x32_10", "noise_words", "uniform_from_words", "gumbel_from_uniform",
     "RowParams", "RowResult", "order_key_sort", "top_k_mask", "top_p_mask",
-    "process_row", "sample_row", "sample", "log_probs", "build_spec_map",
+    "process_row", "sample_row", "sample", "raw_log_probs_at", "log_probs", "build_spec_map",
     "GREEDY_T_MAX", "TOP_P_EPS", "NEAR_TIE_REL",
 ]

@@ -282,6 +282,29 @@ def log_probs(logits, n: int, params: dict, *, gather_indices=None, token_to_req
     return np.array(out)
 
 
+def raw_log_probs_at(logits, n: int, token_ids, *, gather_indices=None,
+                     rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Log-softmax of the raw row (no temperature, no filter) at token_ids[r]:
+    the selected-token log-probs that the TokenSpeed Triton sampling backend
+    page writes from the logits and the sampled ids.  NaN reads as -inf; a -inf
+    entry at the id gives -inf; an id outside the row or a row with no finite
+    logit gives NaN."""
+    logits = np.asarray(logits)
+    out = []
+    for r in (range(n) if rows is None else rows):
+        src = int(gather_indices[r]) if gather_indices is not None else r
+        x = canonical_logits(logits[src])
+        j = int(token_ids[r])
+        fin = x > -np.inf
+        if not fin.any() or j < 0 or j >= x.size:
+            out.append(np.nan)
+            continue
+        m = np.max(x[fin])
+        lse = m + np.log(np.sum(np.exp(x[fin] - m)))
+        out.append(x[j] - lse if x[j] > -np.inf else -np.inf)
+    return np.array(out)
+
+
 def build_spec_map(num_decode: int, num_prefill: int, num_spec: int) -> np.ndarray:
     """Per-row request index of the speculative-verify layout.
 

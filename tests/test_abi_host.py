@@ -110,3 +110,26 @@ def test_spec_map_on_host(lib):
     assert lib.ts_build_spec_map(2, 2, 3, buf, 4, 0, None, ctypes.byref(got)) == tsa.TS_E_SIZE
     assert got.value == 10
     assert lib.ts_build_spec_map(-1, 2, 3, buf, 4, 0, None, ctypes.byref(got)) == tsa.TS_E_ARG
+
+
+def test_raw_log_probs_argument_checks_on_validation_handle(lib):
+    h = ctypes.c_void_p()
+    assert lib.ts_create(100, 8, -1, ctypes.byref(h)) == tsa.TS_OK
+    try:
+        def call(logits=FAKE, dtype=tsa.TS_BF16, rows=8, stride=100, n=8, gather=None, ids=FAKE,
+                 out=FAKE):
+            return lib.ts_raw_log_probs_at(h, logits, dtype, rows, stride, n, gather, ids, out, None)
+        assert call() == tsa.TS_E_HIP                      # all checks pass, no GPU on this handle
+        assert call(n=0) == tsa.TS_OK
+        assert call(dtype=7) == tsa.TS_E_DTYPE
+        assert call(n=9) == tsa.TS_E_SIZE
+        assert call(stride=99) == tsa.TS_E_SIZE
+        assert call(rows=4) == tsa.TS_E_SIZE
+        assert call(rows=4, gather=FAKE) == tsa.TS_E_HIP
+        assert call(logits=None) == tsa.TS_E_ARG
+        assert call(ids=None) == tsa.TS_E_ARG
+        assert call(out=None) == tsa.TS_E_ARG
+        assert lib.ts_raw_log_probs_at(None, FAKE, 0, 8, 100, 8, None, FAKE, FAKE,
+                                       None) == tsa.TS_E_ARG
+    finally:
+        lib.ts_destroy(h)

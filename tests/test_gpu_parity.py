@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 import token_sampling_scaled_amd as tsa
 from tests import parity
@@ -142,6 +143,45 @@ def test_graph_replay_with_device_offsets(name, rows, vocab):
         rep.check()
         seen.add(tuple(got_ids.tolist()))
     assert len(seen) > 1
+
+
+@pytest.mark.parametrize("name,rows,vocab", [("tiny_joint", None, None), ("none_32k", 16, 32000),
+                                             ("topk_128k", 12, 20011), ("topp_152k", 8, 30000),
+                                             ("spec_mix", 24, 16384), ("joint_128k", None, None)])
+def test_raw_log_probs_at(name, rows, vocab):
+    """Log-softmax of the raw rows at given ids (sampled ids, random ids, and
+    ids outside the row), against the oracle within 1e-4."""
+    wl = synth.make(name, rows=rows, vocab=vocab)
+    print(f"[case] raw log-probs {name} rows={wl.n} vocab={wl.vocab}", flush=True)
+    dev = parity.to_device(wl)
+    s = tsa.Sampler(wl.vocab, wl.n)
+    ids, _ = parity.gpu_sample(wl, s, dev)
+    rng = np.random.default_rng(7)
+    for tok in (ids, rng.integers(0, wl.vocab, wl.n).astype(np.int32),
+                np.where(np.arange(wl.n) % 3 == 0, -1, wl.vocab).astype(np.int32)):
+        got = s.raw_log_probs_at(dev["logits"], torch.from_numpy(tok).cuda(), n=wl.n,
+                                 gather_indices=dev["gather"])
+        got = got.cpu().numpy()
+        gi = None if wl.gather_indices is None else wl.gather_indices.numpy()
+        want = oracle.raw_log_probs_at(wl.logits_f64(), wl.n, tok, gather_indices=gi)
+        assert np.array_equal(np.isnan(got), np.isnan(want))
+        assert np.array_equal(np.isneginf(got), np.isneginf(want))
+        fin = np.isfinite(want)
+        assert np.max(np.abs(got[fin] - want[fin]), initial=0.0) <= parity.LP_ATOL
+
+
+def test_raw_log_probs_at_odd_rows():
+    rows = [[1.0, np.nan, -np.inf, 2.0, 0.5, -1.0, 3.0, 0.0]] * 5 + [[-np.inf] * 8]
+    for dtype in (torch.float32, torch.bfloat16):
+        x = torch.tensor(np.array(rows, dtype=np.float32)).to(dtype)
+        tok = np.array([0, 1, 2, -1, 6, 3], dtype=np.int32)
+        s = tsa.Sampler(8, 6)
+        got = s.raw_log_probs_at(x.cuda(), torch.from_numpy(tok).cuda()).cpu().numpy()
+        want = oracle.raw_log_probs_at(x.float().numpy().astype(np.float64), 6, tok)
+        assert np.array_equal(np.isnan(got), np.isnan(want))
+        assert np.array_equal(np.isneginf(got), np.isneginf(want))
+        fin = np.isfinite(want)
+        assert np.max(np.abs(got[fin] - want[fin])) <= parity.LP_ATOL
 
 
 def _custom(rows, dtype=torch.float32, k=0, p=1.0, t=1.0, no_top_k=None, no_top_p=None,

@@ -238,6 +238,29 @@ def test_per_request_offsets_add_to_the_call_offset():
     assert len(draws) > 5
 
 
+def test_raw_log_probs_at_pins():
+    """Log-softmax of the raw row: a worked example, normalisation, shift
+    invariance, the special cases, and agreement with the processed
+    distribution when no filter and T = 1 leave the row as it is."""
+    x = np.array([[0.0, math.log(3.0)]])
+    got = oracle.raw_log_probs_at(np.repeat(x, 2, 0), 2, [1, 0])
+    assert np.allclose(got, [math.log(0.75), -math.log(4.0)], rtol=0, atol=1e-15)
+    rng = np.random.default_rng(21)
+    row = rng.normal(0, 3, size=(1, 200))
+    every = np.array([oracle.raw_log_probs_at(row, 1, [j])[0] for j in range(200)])
+    assert abs(np.sum(np.exp(every)) - 1.0) < 1e-12
+    shifted = np.array([oracle.raw_log_probs_at(row + 123.25, 1, [j])[0] for j in range(200)])
+    assert np.allclose(shifted, every, rtol=0, atol=1e-11)
+    params = {"temperature": np.ones(1), "top_k": np.zeros(1, dtype=np.int64),
+              "top_p": np.ones(1), "seed": np.zeros(1, dtype=np.uint64)}
+    assert np.allclose(oracle.log_probs(row, 1, params)[0], every, rtol=0, atol=1e-12)
+    odd = np.array([[1.0, np.nan, -np.inf, 2.0]] * 5 + [[-np.inf] * 4])
+    got = oracle.raw_log_probs_at(odd, 6, [0, 1, 2, -1, 4, 3])
+    want0 = 1.0 - math.log(math.e + math.e ** 2)
+    assert abs(got[0] - want0) < 1e-15 and got[1] == -np.inf and got[2] == -np.inf
+    assert np.isnan(got[3]) and np.isnan(got[4]) and np.isnan(got[5])
+
+
 def test_near_tie_is_flagged_with_both_alternatives():
     j = np.arange(6)
     g = philox.gumbel_from_uniform(philox.uniform_from_words(philox.noise_words(3, 0, 0, j)))

@@ -63,13 +63,15 @@ def library() -> ctypes.CDLL:
                               ctypes.POINTER(_Params), c_u64, c_i32, c_i32, c_vp, c_vp, c_vp]
     lib.ts_log_probs.argtypes = [c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_vp, c_vp,
                                  ctypes.POINTER(_Params), c_i32, c_i32, c_vp, c_vp, c_vp]
+    lib.ts_raw_log_probs_at.argtypes = [c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_vp, c_vp,
+                                        c_vp, c_vp]
     lib.ts_build_spec_map.argtypes = [c_i32, c_i32, c_i32, c_vp, c_i32, c_i32, c_vp,
                                       ctypes.POINTER(c_i32)]
     lib.ts_select_route.argtypes = [c_i32, c_i32]
     lib.ts_status_str.argtypes = [c_i32]
     lib.ts_status_str.restype = ctypes.c_char_p
-    for name in ("ts_create", "ts_destroy", "ts_sample", "ts_log_probs", "ts_build_spec_map",
-                 "ts_select_route"):
+    for name in ("ts_create", "ts_destroy", "ts_sample", "ts_log_probs", "ts_raw_log_probs_at",
+                 "ts_build_spec_map", "ts_select_route"):
         getattr(lib, name).restype = ctypes.c_int32
     _lib = lib
     return lib
@@ -241,6 +243,25 @@ class Sampler:
                                       int(bool(no_top_p)), _ptr(ids), _ptr(output), _stream(dev)),
                "ts_log_probs")
         return output
+
+
+    def raw_log_probs_at(self, logits: torch.Tensor, token_ids: torch.Tensor, *,
+                         n: Optional[int] = None, gather_indices: Optional[torch.Tensor] = None,
+                         output: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """[n] log-softmax of the raw rows (no temperature, no filter) at token_ids."""
+        dt, rows, stride = _logits_args(logits, self.vocab)
+        dev = logits.device
+        n = rows if n is None else int(n)
+        gather = _index_i32(gather_indices, "gather_indices", n, dev)
+        ids = _index_i32(token_ids, "token_ids", n, dev)
+        if output is None:
+            output = torch.empty(n, dtype=torch.float32, device=dev)
+        elif output.dtype != torch.float32 or output.numel() < n or not output.is_contiguous():
+            raise ValueError("output must be a contiguous float32 tensor with >= n entries")
+        _check(library().ts_raw_log_probs_at(self._h, _ptr(logits), dt, rows, stride, n,
+                                             _ptr(gather), _ptr(ids), _ptr(output), _stream(dev)),
+               "ts_raw_log_probs_at")
+        return output[:n]
 
 
 def build_spec_map(num_decode: int, num_prefill: int, num_spec: int, device=None):

@@ -72,6 +72,9 @@ hipError_t launch_rows(const RowArgs& a, DType dtype, Route route, OutMode mode,
 // Split-row kernel for calls whose every row is unfiltered (no-filter route).
 bool split_none_supported(const RowArgs& a);
 hipError_t launch_rows_split_none(const RowArgs& a, DType dtype, hipStream_t stream);
+// Log-softmax of the raw rows at token_ids (same split kernel without noise);
+// needs split_none_supported(a).
+hipError_t launch_rows_raw_log_prob_at(const RowArgs& a, DType dtype, hipStream_t stream);
 
 // Top-p route: a cutoff kernel (one workgroup per row) and a split draw kernel.
 bool topp_supported(const RowArgs& a);

@@ -22,8 +22,10 @@ namespace {
 using namespace split;
 
 // PT: 4-entry groups per thread; S workgroups per row (gridDim.x = n * S,
-// part-major: workgroup b takes row b % n, part b / n).
-template <typename T, bool VEC, int PT>
+// part-major: workgroup b takes row b % n, part b / n).  RAW: no noise and no
+// temperature; the merge writes the log-softmax of the raw row at
+// token_ids[r] (out_lp[r]) instead of a sample.
+template <typename T, bool VEC, int PT, bool RAW>
 __global__ __launch_bounds__(kSplitBlock) void rows_split_none_kernel(RowArgs a, int32_t S) {
   using E = SplitElem<T>;
   using K = typename E::Key;
@@ -44,9 +46,9 @@ __global__ __launch_bounds__(kSplitBlock) void rows_split_none_kernel(RowArgs a,
   const int32_t per_part = (groups + S - 1) / S;
   const int32_t g_begin = part * per_part;
   const int32_t g_end = g_begin + per_part < groups ? g_begin + per_part : groups;
-  const float temp = a.temperature[q];
-  const uint64_t seed = a.seed[q];
-  const bool greedy = !(temp >= 1e-5f);
+  const float temp = RAW ? 1.0f : a.temperature[q];
+  const uint64_t seed = RAW ? 0ull : a.seed[q];
+  const bool greedy = !RAW && !(temp >= 1e-5f);
   // base-2 units: s2 = x * log2(e) / T.  The Gumbel race is run as
   // argmax (s2 - log2(-log2 u)), which is argmax (x/T - ln(-ln u)) scaled by
   // log2(e) and shifted by a constant; the log-sum-exp uses exp2.
@@ -109,15 +111,21 @@ __global__ __launch_bounds__(kSplitBlock) void rows_split_none_kernel(RowArgs a,
         mloc = fmaxf(mloc, sv[i][e]);
       }
     }
-    const uint64_t off = noise_offset(a, q);
+    float sum = 0.0f;
+    if constexpr (RAW) {
+#pragma unroll
+      for (int i = 0; i < PT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum += __builtin_amdgcn_exp2f(sv[i][e] - mloc);   // 0 for -inf
+    }
+    const uint64_t off = RAW ? 0ull : noise_offset(a, q);
     const NoiseStream ns{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
                          (uint32_t)off, (uint32_t)(off >> 32)};
-    float sum = 0.0f;
     float bz = -__builtin_inff();
     int32_t bj = 0x7FFFFFFF;
     float bs = 0.0f;
 #pragma unroll
-    for (int i = 0; i < PT; ++i) {
+    for (int i = 0; i < (RAW ? 0 : PT); ++i) {
       const int32_t g = g_begin + tid + i * kSplitBlock;
       const Philox4 w = ns.block((uint32_t)g);
 #pragma unroll
@@ -190,7 +198,20 @@ __global__ __launch_bounds__(kSplitBlock) void rows_split_none_kernel(RowArgs a,
     if (beats(bb.o, bb.j, b.o, b.j)) b = bb;
     l = lse_merge(l, ll);
   }
-  if (lane == 0) {
+  if (RAW && lane == 0) {
+    // log-softmax of the raw row at the given id: NaN for an id outside the
+    // row or a row with no finite entry, -inf at a NaN or -inf entry
+    const int64_t j = a.token_ids[r];
+    float out = __builtin_nanf("");
+    if (j >= 0 && j < v && l.m > -__builtin_inff()) {
+      const float x = E::value(E::raw_at(row, j));
+      out = x == x ? (x * 1.4426950408889634f - l.m - __builtin_amdgcn_logf(l.sum)) *
+                         0.69314718055994531f
+                   : -__builtin_inff();
+    }
+    a.out_lp[r] = out;
+    __hip_atomic_store(a.split_counter + r, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (lane == 0) {
     if (b.j == 0x7FFFFFFF) {
       a.out_ids[r] = -1;
       if (a.out_lp) a.out_lp[r] = __builtin_nanf("");
@@ -203,21 +224,45 @@ __global__ __launch_bounds__(kSplitBlock) void rows_split_none_kernel(RowArgs a,
   }
 }
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool RAW>
 hipError_t launch_pt(const RowArgs& a, int32_t S, int pt, hipStream_t stream) {
   const dim3 grid((uint32_t)a.n * (uint32_t)S), block(kSplitBlock);
   switch (pt) {
     case 4:
-      hipLaunchKernelGGL((rows_split_none_kernel<T, VEC, 4>), grid, block, 0, stream, a, S);
+      hipLaunchKernelGGL((rows_split_none_kernel<T, VEC, 4, RAW>), grid, block, 0, stream, a, S);
       break;
     case 8:
-      hipLaunchKernelGGL((rows_split_none_kernel<T, VEC, 8>), grid, block, 0, stream, a, S);
+      hipLaunchKernelGGL((rows_split_none_kernel<T, VEC, 8, RAW>), grid, block, 0, stream, a, S);
       break;
     default:
-      hipLaunchKernelGGL((rows_split_none_kernel<T, VEC, 16>), grid, block, 0, stream, a, S);
+      hipLaunchKernelGGL((rows_split_none_kernel<T, VEC, 16, RAW>), grid, block, 0, stream, a, S);
       break;
   }
   return hipGetLastError();
+}
+
+template <bool RAW>
+hipError_t launch_split(const RowArgs& a, DType dtype, hipStream_t stream) {
+  if (a.n <= 0) return hipSuccess;
+  const int64_t groups = (a.vocab + 3) >> 2;
+  // with noise (VALU-bound) about 4 groups (16 entries) per thread; without
+  // (HBM-bound) about 16, so fewer workgroups merge; at most kMaxSplit parts
+  constexpr int kPer = RAW ? 16 : 4;
+  int64_t s = (groups + kPer * kSplitBlock - 1) / (kPer * kSplitBlock);
+  if (s > kMaxSplit) s = kMaxSplit;
+  if (s < 1) s = 1;
+  const int64_t per_part = (groups + s - 1) / s;
+  const int64_t per_thread = (per_part + kSplitBlock - 1) / kSplitBlock;
+  const int pt = per_thread <= 4 ? 4 : per_thread <= 8 ? 8 : 16;
+  const uintptr_t base = reinterpret_cast<uintptr_t>(a.logits);
+  if (dtype == kF32) {
+    const bool vec = (base % 16) == 0 && (a.row_stride % 4) == 0 && (a.vocab % 4) == 0;
+    return vec ? launch_pt<float, true, RAW>(a, (int32_t)s, pt, stream)
+               : launch_pt<float, false, RAW>(a, (int32_t)s, pt, stream);
+  }
+  const bool vec = (base % 8) == 0 && (a.row_stride % 4) == 0 && (a.vocab % 4) == 0;
+  return vec ? launch_pt<uint16_t, true, RAW>(a, (int32_t)s, pt, stream)
+             : launch_pt<uint16_t, false, RAW>(a, (int32_t)s, pt, stream);
 }
 
 }  // namespace
@@ -230,24 +275,11 @@ bool split_none_supported(const RowArgs& a) {
 }
 
 hipError_t launch_rows_split_none(const RowArgs& a, DType dtype, hipStream_t stream) {
-  if (a.n <= 0) return hipSuccess;
-  const int64_t groups = (a.vocab + 3) >> 2;
-  // about 4 groups (16 entries) per thread, at most kMaxSplit parts per row
-  int64_t s = (groups + 4 * kSplitBlock - 1) / (4 * kSplitBlock);
-  if (s > kMaxSplit) s = kMaxSplit;
-  if (s < 1) s = 1;
-  const int64_t per_part = (groups + s - 1) / s;
-  const int64_t per_thread = (per_part + kSplitBlock - 1) / kSplitBlock;
-  const int pt = per_thread <= 4 ? 4 : per_thread <= 8 ? 8 : 16;
-  const uintptr_t base = reinterpret_cast<uintptr_t>(a.logits);
-  if (dtype == kF32) {
-    const bool vec = (base % 16) == 0 && (a.row_stride % 4) == 0 && (a.vocab % 4) == 0;
-    return vec ? launch_pt<float, true>(a, (int32_t)s, pt, stream)
-               : launch_pt<float, false>(a, (int32_t)s, pt, stream);
-  }
-  const bool vec = (base % 8) == 0 && (a.row_stride % 4) == 0 && (a.vocab % 4) == 0;
-  return vec ? launch_pt<uint16_t, true>(a, (int32_t)s, pt, stream)
-             : launch_pt<uint16_t, false>(a, (int32_t)s, pt, stream);
+  return launch_split<false>(a, dtype, stream);
+}
+
+hipError_t launch_rows_raw_log_prob_at(const RowArgs& a, DType dtype, hipStream_t stream) {
+  return launch_split<true>(a, dtype, stream);
 }
 
 }  // namespace tss

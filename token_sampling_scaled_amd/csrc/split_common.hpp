@@ -25,6 +25,9 @@ struct SplitElem<float> {
   using Packed = u32x4;
   static constexpr uint32_t kNegInfRaw = 0xFF800000u;
   __device__ __forceinline__ static float value(uint32_t raw) { return __uint_as_float(raw); }
+  __device__ __forceinline__ static uint32_t raw_at(const void* row, int64_t j) {
+    return __float_as_uint(static_cast<const float*>(row)[j]);
+  }
   // Entries j0 .. j0+3, present and 16-byte aligned.
   __device__ __forceinline__ static Packed load_packed(const void* row, int64_t j0) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
@@ -51,6 +54,9 @@ struct SplitElem<uint16_t> {
   using Packed = u32x2;
   static constexpr uint32_t kNegInfRaw = 0xFF80u;
   __device__ __forceinline__ static float value(uint32_t raw) { return __uint_as_float(raw << 16); }
+  __device__ __forceinline__ static uint32_t raw_at(const void* row, int64_t j) {
+    return static_cast<const uint16_t*>(row)[j];
+  }
   __device__ __forceinline__ static Packed load_packed(const void* row, int64_t j0) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
         reinterpret_cast<const uint16_t*>(row) + j0));

@@ -46,11 +46,10 @@ struct DeviceGuard {
   }
 };
 
-ts_status check_common(const ts_sampler* s, const void* logits, ts_dtype dtype,
-                       int64_t rows_in_buffer, int64_t row_stride, int32_t n,
-                       const int32_t* gather, const int32_t* map, const ts_params* params,
-                       int32_t no_top_k, int32_t no_top_p) {
-  if (s == nullptr || params == nullptr) return TS_E_ARG;
+// The logits buffer and row selection of a call.
+ts_status check_rows(const ts_sampler* s, const void* logits, ts_dtype dtype,
+                     int64_t rows_in_buffer, int64_t row_stride, int32_t n, const int32_t* gather) {
+  if (s == nullptr) return TS_E_ARG;
   if (dtype != TS_F32 && dtype != TS_BF16) return TS_E_DTYPE;
   if (n < 0 || rows_in_buffer < 0) return TS_E_ARG;
   if (n > s->max_rows) return TS_E_SIZE;
@@ -58,6 +57,16 @@ ts_status check_common(const ts_sampler* s, const void* logits, ts_dtype dtype,
   if (gather == nullptr && rows_in_buffer < n) return TS_E_SIZE;
   if (n == 0) return TS_OK;
   if (logits == nullptr || rows_in_buffer == 0) return TS_E_ARG;
+  return TS_OK;
+}
+
+ts_status check_common(const ts_sampler* s, const void* logits, ts_dtype dtype,
+                       int64_t rows_in_buffer, int64_t row_stride, int32_t n,
+                       const int32_t* gather, const int32_t* map, const ts_params* params,
+                       int32_t no_top_k, int32_t no_top_p) {
+  if (params == nullptr) return TS_E_ARG;
+  const ts_status st = check_rows(s, logits, dtype, rows_in_buffer, row_stride, n, gather);
+  if (st != TS_OK || n == 0) return st;
   if (params->temperature == nullptr || params->seed == nullptr) return TS_E_ARG;
   if (params->num_requests < 1) return TS_E_ARG;
   if (map == nullptr && params->num_requests < n) return TS_E_SIZE;
@@ -219,6 +228,33 @@ ts_status ts_log_probs(ts_sampler* s, const void* logits, ts_dtype dtype, int64_
   const hipError_t err =
       tss::launch_rows(a, dtype == TS_F32 ? tss::kF32 : tss::kBF16, route,
                        token_ids ? tss::kOutLogProbAt : tss::kOutLogProbFull, (hipStream_t)stream);
+  return err == hipSuccess ? TS_OK : TS_E_HIP;
+}
+
+ts_status ts_raw_log_probs_at(ts_sampler* s, const void* logits, ts_dtype dtype,
+                              int64_t rows_in_buffer, int64_t row_stride, int32_t n,
+                              const int32_t* gather_indices, const int32_t* token_ids, float* out,
+                              void* stream) {
+  ts_status st = check_rows(s, logits, dtype, rows_in_buffer, row_stride, n, gather_indices);
+  if (st != TS_OK) return st;
+  if (n == 0) return TS_OK;
+  if (token_ids == nullptr || out == nullptr) return TS_E_ARG;
+  if (s->device < 0) return TS_E_HIP;
+  DeviceGuard guard(s->device);
+  if (!guard.ok) return TS_E_HIP;
+  tss::RowArgs a{};
+  a.logits = logits;
+  a.row_stride = row_stride;
+  a.vocab = s->vocab;
+  a.n = n;
+  a.gather = gather_indices;
+  a.token_ids = token_ids;
+  a.out_lp = out;
+  a.split_counter = s->split_counter;
+  a.split_partials = s->split_partials;
+  if (!tss::split_none_supported(a)) return TS_E_SIZE;
+  const hipError_t err = tss::launch_rows_raw_log_prob_at(a, dtype == TS_F32 ? tss::kF32 : tss::kBF16,
+                                                          (hipStream_t)stream);
   return err == hipSuccess ? TS_OK : TS_E_HIP;
 }
 
