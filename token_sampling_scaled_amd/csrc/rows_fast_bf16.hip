@@ -702,6 +702,20 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
                                                 src * a.row_stride);
   const int nvec = (int)(a.vocab >> 3);
   const int nfull = nvec / kB;       // vector slots every thread of the row holds
+
+  // ---- stream the row into registers.  Slots past the row re-read its last
+  // vector and are ignored where used, so every load is unconditional and
+  // each vector is waited for on its own at its first use.  The first half is
+  // issued before the request's parameters are even read (they decide the
+  // body, and waiting for them first would delay every load by one memory
+  // latency); the second half goes out one load per arriving first-half vector.
+  v4u d[NV];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int vi = i * kB + tid;
+    d[i] = __builtin_nontemporal_load(row + (vi < nvec ? vi : nvec - 1));
+  }
+
   const float temp = a.temperature[q];
   const int32_t kq = kHasK ? a.top_k[q] : 0;
   const float pq = kHasP ? a.top_p[q] : 1.0f;
@@ -719,16 +733,6 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
     return;
   }
 
-  // ---- stream the row into registers.  Slots past the row re-read its last
-  // vector and are ignored where used, so every load is unconditional and
-  // each vector is waited for on its own at its first use.  The first half is
-  // issued now, the second half one load per arriving first-half vector.
-  v4u d[NV];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int vi = i * kB + tid;
-    d[i] = __builtin_nontemporal_load(row + (vi < nvec ? vi : nvec - 1));
-  }
   if (greedy || nok) {
 #pragma unroll
     for (int i = NB; i < NV; ++i) {
