@@ -17,11 +17,12 @@
 //       reaches p Z.  If the bucket holds more entries than LDS does, the same
 //       radix passes read them from the row instead.
 //    The row's cutoff key and the mass of P go to the workspace.
-// 2. rows_topp_draw_kernel, a persistent grid of 256-thread workgroups taking
-//    (row, tile) items from a counter: the members of P (key >= cutoff key)
-//    of a tile are compacted in LDS, their Philox noise is drawn and the
-//    tile's perturbed argmax is kept; the item that finishes a row last merges
-//    the row's tiles and writes id and log-prob.
+// 2. rows_topp_draw_kernel, a grid of 256-thread workgroups taking (row, tile)
+//    items in a fixed interleaved order: the 4-entry groups of a tile that
+//    hold members of P (key >= cutoff key) are compacted in LDS, one Philox
+//    block per group gives its members' noise, and the tile's perturbed argmax
+//    is kept; the item that finishes a row last merges the row's tiles and
+//    writes id and log-prob.
 //
 // Masses are 64-bit fixed-point integers (scale 2^mass_shift, plus one per
 // entry so that a nonzero sum marks a nonempty bin), so every sum is
@@ -404,8 +405,8 @@ __global__ __launch_bounds__(kSplitBlock) void rows_topp_draw_kernel(RowArgs a, 
   using E = SplitElem<T>;
   using K = typename E::Key;
   constexpr int kTile = PT * kSplitBlock;    // groups per tile
-  __shared__ uint32_t mj[kTile * 4];
-  __shared__ float ms[kTile * 4];
+  __shared__ uint32_t mg[kTile];       // member groups: (group << 4) | member mask
+  __shared__ float ms[kTile][4];       // their scaled logits
   __shared__ uint32_t woff[kSplitWaves + 1];
   __shared__ Best sbest[kSplitWaves];
   __shared__ uint32_t sticket;
@@ -455,16 +456,20 @@ __global__ __launch_bounds__(kSplitBlock) void rows_topp_draw_kernel(RowArgs a, 
         }
       }
     }
-    // members of P in this tile (key >= key_c), compacted in LDS
-    uint32_t mask = 0;
+    // 4-entry groups of this tile that hold members of P (key >= key_c),
+    // compacted in LDS: one Philox block per such group gives the noise of all
+    // its members
+    uint32_t gmask[PT];
+    uint32_t cnt = 0;
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       const bool in = t0 + tid + i * kSplitBlock < t_end;
+      gmask[i] = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        mask |= (in && K::from_bits(raw[i][e]) >= key_c ? 1u : 0u) << (i * 4 + e);
+        gmask[i] |= (in && K::from_bits(raw[i][e]) >= key_c ? 1u : 0u) << e;
+      cnt += gmask[i] ? 1u : 0u;
     }
-    const uint32_t cnt = (uint32_t)__popc(mask);
     const uint32_t incl = wave_scan_incl(cnt);
     if (lane == kWave - 1) woff[wid + 1] = incl;
     __syncthreads();
@@ -476,13 +481,11 @@ __global__ __launch_bounds__(kSplitBlock) void rows_topp_draw_kernel(RowArgs a, 
     uint32_t pos = woff[wid] + incl - cnt;
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
+      if (gmask[i]) {
+        mg[pos] = ((uint32_t)(t0 + tid + i * kSplitBlock) << 4) | gmask[i];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if ((mask >> (i * 4 + e)) & 1u) {
-          mj[pos] = (uint32_t)((t0 + tid + i * kSplitBlock) * 4 + e);
-          ms[pos] = E::value(raw[i][e]) * scale2;
-          ++pos;
-        }
+        for (int e = 0; e < 4; ++e) ms[pos][e] = E::value(raw[i][e]) * scale2;
+        ++pos;
       }
     }
     __syncthreads();
@@ -491,14 +494,21 @@ __global__ __launch_bounds__(kSplitBlock) void rows_topp_draw_kernel(RowArgs a, 
     int32_t bj = 0x7FFFFFFF;
     float bs = 0.0f;
     for (uint32_t t = tid; t < nm; t += kSplitBlock) {
-      const uint32_t j = mj[t];
-      const float sv = ms[t];
-      const float u = ((float)(ns.word(j) >> 9) + 0.5f) * 0x1p-23f;
-      const float zz = sv - __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
-      if (better(zz, (int32_t)j, bz, bj)) {
-        bz = zz;
-        bj = (int32_t)j;
-        bs = sv;
+      const uint32_t gm = mg[t];
+      const uint32_t g = gm >> 4;
+      const Philox4 w = ns.block(g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (!((gm >> e) & 1u)) continue;
+        const float sv = ms[t][e];
+        const float u = ((float)(w.v[e] >> 9) + 0.5f) * 0x1p-23f;
+        const float zz = sv - __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
+        const int32_t jj = (int32_t)(g * 4 + e);
+        if (better(zz, jj, bz, bj)) {
+          bz = zz;
+          bj = jj;
+          bs = sv;
+        }
       }
     }
     Best best{0u, 0x7FFFFFFF, 0.0f};
