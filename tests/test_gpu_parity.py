@@ -229,7 +229,8 @@ EDGE_ROWS = {
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("case", sorted(EDGE_ROWS))
 @pytest.mark.parametrize("k,p,t", [(0, 1.0, 1.0), (2, 1.0, 0.8), (0, 0.5, 1.3), (3, 0.7, 1.0),
-                                   (1, 1.0, 1.0), (0, 0.0, 1.0), (0, 1.0, 0.0), (100, 0.9, 1.0)])
+                                   (1, 1.0, 1.0), (0, 0.0, 1.0), (0, 1.0, 0.0), (100, 0.9, 1.0),
+                                   (2, 0.9, 0.0)])
 def test_edge_rows(case, dtype, k, p, t):
     wl = _custom(EDGE_ROWS[case], dtype=dtype, k=k, p=p, t=t)
     print(f"[case] edge {case} {dtype} k={k} p={p} t={t}", flush=True)
@@ -245,7 +246,7 @@ NOK_ROWS = [
 ]
 
 
-@pytest.mark.parametrize("p,t", [(1.0, 1.0), (0.9, 1.0), (0.99, 100.0), (0.0, 0.7)])
+@pytest.mark.parametrize("p,t", [(1.0, 1.0), (0.9, 1.0), (0.99, 100.0), (0.0, 0.7), (0.9, 0.0)])
 def test_joint_route_rows_without_top_k(p, t):
     """bf16 rows on the joint route whose own top-k is off: the register-resident
     body (unfiltered, or top-p by an exact key histogram); a cutoff below its key
