@@ -344,3 +344,74 @@ def test_no_filter_rows_split_over_workgroups(dtype, vocab, stride_pad):
     wl.step_offset = 1
     ids3, lps3 = parity.gpu_sample(wl, s, dev)
     parity.compare_samples(ids3, lps3, parity.oracle_sample(wl)).check()
+
+
+def _mixed_rows_workload(n, vocab, frac_unfiltered, seed, n_req=None, gather_pool=0):
+    """bf16 N(0, 3^2) rows on the joint route; each request is unfiltered with
+    probability frac_unfiltered, else top-k, top-p or both (k ~ U{1..1024},
+    p ~ U[0.5, 0.99], T ~ U[0.5, 1.5]).  With n_req, rows map onto requests."""
+    rng = np.random.default_rng(seed)
+    rows_in_buf = n + gather_pool
+    x = torch.from_numpy(rng.normal(0.0, 3.0, size=(rows_in_buf, vocab)).astype(np.float32)).to(torch.bfloat16)
+    q = n if n_req is None else n_req
+    mode = np.where(rng.random(q) < frac_unfiltered, 0, rng.integers(1, 4, size=q))
+    k = np.where((mode == 1) | (mode == 3), rng.integers(1, 1025, size=q), 0).astype(np.int32)
+    p = np.where(mode >= 2, rng.uniform(0.5, 0.99, size=q), 1.0).astype(np.float32)
+    t = rng.uniform(0.5, 1.5, size=q).astype(np.float32)
+    wl = synth.Workload("mixed", x, n, torch.from_numpy(t), torch.from_numpy(k), torch.from_numpy(p),
+                        torch.arange(q, dtype=torch.int64) * 7 + 3)
+    if n_req is not None:
+        wl.token_to_request_index = torch.from_numpy(rng.integers(0, q, size=n).astype(np.int32))
+    if gather_pool:
+        wl.gather_indices = torch.from_numpy(rng.permutation(rows_in_buf)[:n].astype(np.int32))
+    wl.no_top_k = False
+    wl.no_top_p = False
+    return wl
+
+
+@pytest.mark.parametrize("n,vocab,frac,n_req,pool", [
+    (40, 20000, 0.4, None, 0),       # rows not a multiple of the 16-vector stride
+    (48, 131072, 1.0, None, 0),      # every row unfiltered, the largest register-resident row
+    (96, 65536, 0.3, 32, 16),        # request map and gather
+    (1100, 2048, 0.3, None, 0),      # more rows than a workgroup has threads
+    (300, 8192, 0.4, 100, 20),       # more rows than CUs: heavy rows are started first
+])
+def test_unfiltered_rows_in_mixed_batches(n, vocab, frac, n_req, pool):
+    """Joint-route bf16 calls whose rows mix unfiltered, top-k-only,
+    top-p-only and joint requests (ragged last vectors, request maps, gather,
+    more rows than one workgroup has threads).  Calls in a row on one handle,
+    with step offsets 0, 1, 0, each write every output (the buffers are
+    filled with sentinels first) and give the oracle's results for their
+    offset, so no state carries over between calls."""
+    wl = _mixed_rows_workload(n, vocab, frac, seed=n + vocab, n_req=n_req, gather_pool=pool)
+    print(f"[case] mixed unfiltered n={n} vocab={vocab} frac={frac}", flush=True)
+    dev = parity.to_device(wl)
+    s = tsa.Sampler(wl.vocab, wl.n)
+    refs = {off: parity.oracle_sample(wl, step_offset=off) for off in (0, 1)}
+    out = torch.empty(n, dtype=torch.int32, device="cuda")
+    lp = torch.empty(n, dtype=torch.float32, device="cuda")
+    got = {}
+    for off in (0, 1, 0):
+        out.fill_(-7)
+        lp.fill_(123.0)
+        s.sample(dev["logits"], n, dev["params"], no_top_k=False, no_top_p=False,
+                 gather_indices=dev["gather"], token_to_request_index=dev["req"],
+                 step_offset=off, output=out, logprob_output=lp)
+        torch.cuda.synchronize()
+        ids, lps = out.cpu().numpy(), lp.cpu().numpy()
+        assert not np.any(ids == -7), "rows left unwritten"
+        parity.compare_samples(ids, lps, refs[off]).check()
+        if off in got:
+            assert np.array_equal(ids, got[off][0])
+            assert np.array_equal(lps, got[off][1], equal_nan=True)
+        got[off] = (ids, lps)
+    assert not np.array_equal(got[0][0], got[1][0])
+
+
+def test_log_probs_with_more_rows_than_cus():
+    """Full-row log-probs on the joint route with more rows than the device has
+    CUs (the workgroups take the rows without a top-k body first)."""
+    wl = _mixed_rows_workload(300, 4096, 0.3, seed=77, n_req=120, gather_pool=10)
+    print(f"[case] log_probs mixed rows={wl.n} vocab={wl.vocab}", flush=True)
+    gpu = parity.gpu_log_probs(wl)
+    parity.compare_log_probs(gpu, parity.oracle_log_probs(wl), parity.oracle_sample(wl)).check()

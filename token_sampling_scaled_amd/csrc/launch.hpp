@@ -57,6 +57,8 @@ struct RowArgs {
   uint32_t* split_counter;     // workspace: [max_rows] zeros between calls
   void* split_partials;        // workspace: [max_rows * kMaxSplit] SplitPartial
   TopPRow* topp_rows;          // workspace: [max_rows]
+  int32_t heavy_first;         // fast kernel: workgroups take the rows without a register-
+                               // resident top-k body first (more rows than CUs, n <= 1024)
 };
 
 // Philox offset of request q in this call.

@@ -676,6 +676,60 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
   return true;
 }
 
+// The row of this workgroup when a call has more rows than the device has
+// CUs: one workgroup of this kernel fills a CU, so the rows of the workgroups
+// dispatched last start only when earlier ones end.  Rows that take the
+// register-resident top-k body (or greedy sampling) end within a few
+// microseconds of their data; the others (no top-k: Philox noise for the
+// whole row or its nucleus; k > 1024, greedy log-probs: the general body) can
+// take several times as long.  So workgroup b takes the b-th heavy row (in
+// row order), and after the heavy rows the light ones: a permutation of the
+// rows that changes no result, only the order rows start in.  Needs n <= 1024
+// (one row per thread of the classification).
+template <int ROUTE, int MODE>
+__device__ __forceinline__ int heavy_first_row(const RowArgs& a, uint64_t* cls) {
+  constexpr bool kHasK = (ROUTE == kRouteTopK || ROUTE == kRouteJoint);
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
+  bool heavy = false;
+  if (tid < a.n) {
+    const int64_t qt = a.req_map ? (int64_t)a.req_map[tid] : (int64_t)tid;
+    const float t = a.temperature[qt];
+    const int32_t k = kHasK ? a.top_k[qt] : 0;
+    const bool greedy = !(t >= 1e-5f);
+    const bool light = greedy ? MODE == kOutSample
+                              : (kHasK && k >= 1 && (int64_t)k < a.vocab && k <= kMaxK);
+    heavy = !light;
+  }
+  const uint64_t bm = __ballot(heavy);
+  if (lane == 0) cls[wid] = bm;
+  __syncthreads();
+  uint32_t nh = 0;
+#pragma unroll
+  for (int w = 0; w < kWv; ++w) nh += (uint32_t)__popcll(cls[w]);
+  const uint32_t b = blockIdx.x;
+  const bool want_heavy = b < nh;
+  uint32_t idx = want_heavy ? b : b - nh;       // rank of the row within its class
+  int r = -1;
+#pragma unroll
+  for (int w = 0; w < kWv; ++w) {
+    const int left = a.n - w * kWave;           // rows of this wave's slice
+    const uint64_t valid = left >= kWave ? ~0ull : (left <= 0 ? 0ull : ((1ull << left) - 1ull));
+    const uint64_t m = want_heavy ? cls[w] : (~cls[w] & valid);
+    const uint32_t c = (uint32_t)__popcll(m);
+    if (r < 0) {
+      if (idx < c) {
+        const unsigned long long hit = __ballot(((m >> lane) & 1ull) && lane_rank(m) == idx);
+        r = w * kWave + (__ffsll((long long)hit) - 1);
+      } else {
+        idx -= c;
+      }
+    }
+  }
+  return r >= 0 ? r : (int)blockIdx.x;   // always found: b < n and the classes split [0, n)
+}
+
 template <int NV, int ROUTE, int MODE>
 __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   constexpr bool kHasK = (ROUTE == kRouteTopK || ROUTE == kRouteJoint);
@@ -690,9 +744,10 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   constexpr int NG = NQ / GV;
   constexpr uint32_t kDiv = 8u * NV / NQ;   // c ~ 2k * (share of the row in the sample)
   __shared__ RowShared sh;
+  __shared__ uint64_t cls[kWv];
   FastShared& fs = sh.f;
 
-  const int r = blockIdx.x;
+  const int r = a.heavy_first ? heavy_first_row<ROUTE, MODE>(a, cls) : (int)blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wid = tid / kWave;

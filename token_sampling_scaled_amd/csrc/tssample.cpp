@@ -19,6 +19,7 @@ struct ts_sampler {
   uint32_t* split_counter;
   void* split_partials;
   tss::TopPRow* topp_rows;
+  int32_t num_cu;        // compute units of the device (0 for a validation-only handle)
 };
 
 namespace {
@@ -94,6 +95,9 @@ tss::RowArgs make_args(const ts_sampler* s, const void* logits, int64_t row_stri
   a.split_counter = s->split_counter;
   a.split_partials = s->split_partials;
   a.topp_rows = s->topp_rows;
+  // one fast-kernel workgroup fills a CU: with more rows than CUs the rows
+  // that start late should be the quick ones
+  a.heavy_first = (s->num_cu > 0 && n > s->num_cu && n <= 1024) ? 1 : 0;
   return a;
 }
 
@@ -140,6 +144,7 @@ ts_status ts_create(int64_t vocab, int32_t max_rows, int32_t device, ts_sampler*
   s->split_counter = nullptr;
   s->split_partials = nullptr;
   s->topp_rows = nullptr;
+  s->num_cu = 0;
   if (device >= 0) {
     // counters, padded to 256 bytes, then the partial results, then the
     // per-row top-p state
@@ -149,6 +154,12 @@ ts_status ts_create(int64_t vocab, int32_t max_rows, int32_t device, ts_sampler*
     const size_t bytes = counter_bytes + partial_bytes + topp_bytes;
     DeviceGuard guard(device);
     if (!guard.ok) {
+      delete s;
+      return TS_E_HIP;
+    }
+    if (hipDeviceGetAttribute(&s->num_cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+        s->num_cu < 1) {
+      (void)hipGetLastError();
       delete s;
       return TS_E_HIP;
     }
