@@ -243,6 +243,8 @@ NOK_ROWS = [
     [-np.inf] * 16,                                                      # nothing finite
     [-1.0, -0.0, -2.0, -0.5] * 4,                                        # the maximum is -0
     [0.5] + [-20.0] * 15,                                                # flat at T = 100
+    [-np.nan, 1.0, 0.5, -0.0, 0.0, 2.0, -np.nan, -3.0] * 2,              # negative NaN only
+    [-0.0, 0.0, -0.0, -8.0] * 4,                                         # -0 and +0 in the top group
 ]
 
 

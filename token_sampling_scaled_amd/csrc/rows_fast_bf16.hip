@@ -88,6 +88,7 @@ constexpr int kNoKBins = 32768;
 struct NoKShared {
   uint32_t hist[kNoKBins];
   uint32_t wkey[kWv];
+  uint32_t wnan[kWv];              // lanes of the wave holding a negative NaN
   float wz[kWv];
   uint32_t vc_key;                 // the cutoff group's order key
   float zp;                        // mass of P in units of exp(x_max / T)
@@ -117,6 +118,24 @@ __device__ __forceinline__ uint32_t pk_max_i16(uint32_t a, uint32_t b) {
   const i16x2 x = __builtin_bit_cast(i16x2, a);
   const i16x2 y = __builtin_bit_cast(i16x2, b);
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+
+// Unsigned saturated a - b of both halves: a half is nonzero iff a > b there.
+__device__ __forceinline__ uint32_t pk_sub_sat_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, a),
+                                                                    __builtin_bit_cast(u16x2, b)));
 }
 
 __device__ __forceinline__ int32_t lo_i16(uint32_t u) { return (int32_t)(int16_t)(u & 0xFFFFu); }
@@ -506,6 +525,9 @@ __device__ __forceinline__ float key_value(uint32_t key) {
 // before them stays below p * Z.  Returns false when the row needs the general
 // body instead (NaN or +inf in the row, or a top-p cutoff below the window of
 // 32768 order keys under the row maximum); the caller then synchronises first.
+// Every pass works on the raw order keys of two entries at a time (packed
+// 16-bit maxima, minima and saturated differences); -0 and +0, whose keys
+// differ by one, are told apart only where an entry is counted or drawn.
 template <int NV>
 __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int nfull, const v4u (&d)[NV],
                         float inv_t, bool p_on, float pq, uint64_t seed, uint64_t off,
@@ -514,19 +536,27 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wid = tid / kWave;
-  // ---- row maximum of the order keys (NaN patterns sort outside the finite range)
-  uint32_t kmx = 0;
+  // ---- largest and smallest order key (positive NaN sorts above +inf,
+  // negative NaN below -inf)
+  uint32_t kmx2 = 0u, kmn2 = 0xFFFFFFFFu;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     if (!(i < nfull || i * kB + tid < nvec)) continue;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t k2 = keys2(word_of(d[i], w));
-      kmx = max(kmx, max(canon_key(k2 & 0xFFFFu), canon_key(k2 >> 16)));
+      kmx2 = pk_max_u16(kmx2, k2);
+      kmn2 = pk_min_u16(kmn2, k2);
     }
   }
+  uint32_t kmx = canon_key(max(kmx2 & 0xFFFFu, kmx2 >> 16));
+  const uint32_t kmn = min(kmn2 & 0xFFFFu, kmn2 >> 16);
   kmx = wave_max_dpp(kmx);
-  if (lane == 0) ns_.wkey[wid] = kmx;
+  const uint32_t nan_lo = (uint32_t)__popcll(__ballot(kmn < kNegInfKey));
+  if (lane == 0) {
+    ns_.wkey[wid] = kmx;
+    ns_.wnan[wid] = nan_lo;
+  }
   if (p_on) {                        // clear the histogram meanwhile
     v4u* h4 = reinterpret_cast<v4u*>(ns_.hist);
 #pragma unroll
@@ -534,23 +564,27 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
   }
   __syncthreads();
   kmx = wave_max_dpp(lane < kWv ? ns_.wkey[lane] : 0u);
-  if (kmx >= kPosInfKey) return false;            // NaN or +inf: general body
+  const uint32_t any_nan_lo = wave_max_dpp(lane < kWv ? ns_.wnan[lane] : 0u);
+  if (kmx >= kPosInfKey || any_nan_lo != 0) return false;   // NaN or +inf: general body
   if (kmx <= kNegInfKey) {                        // no finite entry
     if (tid == 0) write_result(a, r, -1, __builtin_nanf(""));
     return true;
   }
+  // base-2 units: s2 = x log2(e) / T; exp2(s2 - m2) = exp(x / T - m)
+  const float sc2 = 1.4426950408889634f * inv_t;
+  const float m2 = key_value(kmx) * sc2;
   const float m = __fmul_rn(key_value(kmx), inv_t);
 
-  // ---- Z = sum over finite entries of exp(x / T - m)
+  // ---- Z = sum over finite entries of exp(x / T - m) (exp2 of -inf is 0)
   float z = 0.0f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     if (!(i < nfull || i * kB + tid < nvec)) continue;
 #pragma unroll
-    for (int sl = 0; sl < 8; ++sl) {
-      const float x = bits_value(elem_i16(d[i], sl) & 0xFFFF);   // any sign
-      const float e = __expf(__fmaf_rn(x, inv_t, -m));
-      z += (x > -__builtin_inff()) ? e : 0.0f;                   // NaN and -inf drop out
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t u = word_of(d[i], w);
+      z += __builtin_amdgcn_exp2f(__fmaf_rn(__uint_as_float(u << 16), sc2, -m2));
+      z += __builtin_amdgcn_exp2f(__fmaf_rn(__uint_as_float(u & 0xFFFF0000u), sc2, -m2));
     }
   }
   z = wave_sum(z);
@@ -565,20 +599,30 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
   if (p_on) {
     // ---- exact histogram of the entries in the window that can be in P:
     // the entries with s < m + ln((1 - p) Z / V) weigh less than (1 - p) Z
-    // together, so the cutoff is never below them
+    // together, so the cutoff is never below them.  The smallest order key
+    // whose value passes that test (a binary search: the test is monotone in
+    // the key, and -0 passes exactly when +0 does) bounds the counted keys.
     const uint32_t wlo = kmx > (uint32_t)(kNoKBins - 1) ? kmx - (uint32_t)(kNoKBins - 1) : 1u;
     const float s_lo = m + __logf(fmaxf(1.0f - pq, 0.0f) * z / (float)a.vocab);
+    uint32_t klo = max(wlo, kNegInfKey + 1), khi = kmx;   // kmx itself always passes
+    while (klo < khi) {
+      const uint32_t mid = (klo + khi) >> 1;
+      if (__fmul_rn(key_value(mid), inv_t) >= s_lo) khi = mid;
+      else klo = mid + 1;
+    }
+    const uint32_t kthr = klo;
+    const i16x2 below2 = __builtin_bit_cast(i16x2, (kthr - 1u) * 0x10001u);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       if (!(i < nfull || i * kB + tid < nvec)) continue;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t k2 = keys2(word_of(d[i], w));
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t key = canon_key(h ? (k2 >> 16) : (k2 & 0xFFFFu));
-          if (key >= wlo && key > kNegInfKey && __fmul_rn(key_value(key), inv_t) >= s_lo)
-            atomicAdd(&ns_.hist[key - wlo], 1u);
+        // halves >= kthr leave a nonzero unsigned saturated difference
+        const uint32_t hit = pk_sub_sat_u16(k2, __builtin_bit_cast(uint32_t, below2));
+        if (hit) {
+          if (hit & 0xFFFFu) atomicAdd(&ns_.hist[canon_key(k2 & 0xFFFFu) - wlo], 1u);
+          if (hit >> 16) atomicAdd(&ns_.hist[canon_key(k2 >> 16) - wlo], 1u);
         }
       }
     }
@@ -600,7 +644,8 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
         for (int i = 0; i < 4; ++i) {
           const int32_t b = top - (4 * lane + i);
           cc[i] = b >= (int32_t)wlo ? ns_.hist[b - (int32_t)wlo] : 0u;
-          mm[i] = cc[i] ? (float)cc[i] * __expf(__fmaf_rn(key_value((uint32_t)b), inv_t, -m)) : 0.0f;
+          mm[i] = cc[i] ? (float)cc[i] * __builtin_amdgcn_exp2f(__fmaf_rn(key_value((uint32_t)b), sc2, -m2))
+                        : 0.0f;
           ms += mm[i];
         }
         const float mi = wave_scan_f32(ms);
@@ -638,9 +683,12 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
     zp = ns_.zp;
   }
 
-  // ---- Philox noise for the members of P (key >= vc_key), perturbed argmax
+  // ---- Philox noise for the members of P (canonical key >= vc_key: raw key
+  // >= vc_key, and -0 too when the cutoff group is +0's), perturbed argmax
   const NoiseStream nst{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
                         (uint32_t)off, (uint32_t)(off >> 32)};
+  const uint32_t raw_thr = vc_key == kPosZeroKey ? kNegZeroKey : vc_key;
+  const uint32_t below_m = (raw_thr - 1u) * 0x10001u;
   Pick best{-__builtin_inff(), 0x7FFFFFFF, 0.0f};
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -651,16 +699,11 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
       // entries 4h .. 4h + 3 of the vector: one Philox block
       const uint32_t k2a = keys2(word_of(d[i], 2 * h));
       const uint32_t k2b = keys2(word_of(d[i], 2 * h + 1));
-      const uint32_t kk[4] = {canon_key(k2a & 0xFFFFu), canon_key(k2a >> 16),
-                              canon_key(k2b & 0xFFFFu), canon_key(k2b >> 16)};
-      bool mem[4];
-      bool any = false;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        mem[e] = kk[e] >= vc_key && kk[e] <= kPosInfKey;
-        any |= mem[e];
-      }
-      if (!any) continue;
+      const uint32_t ha = pk_sub_sat_u16(k2a, below_m);
+      const uint32_t hb = pk_sub_sat_u16(k2b, below_m);
+      if ((ha | hb) == 0) continue;
+      const uint32_t kk[4] = {k2a & 0xFFFFu, k2a >> 16, k2b & 0xFFFFu, k2b >> 16};
+      const bool mem[4] = {(ha & 0xFFFFu) != 0, (ha >> 16) != 0, (hb & 0xFFFFu) != 0, (hb >> 16) != 0};
       const Philox4 wds = nst.block((uint32_t)(2 * vi + h));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
