@@ -1063,8 +1063,12 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
       float o[8];
 #pragma unroll
       for (int sl = 0; sl < 8; ++sl) o[sl] = lp_of(elem_i16(d[i], sl), (uint32_t)(vi * 8 + sl));
-      __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, out_row + 2 * vi);
-      __builtin_nontemporal_store(f32x4{o[4], o[5], o[6], o[7]}, out_row + 2 * vi + 1);
+      // plain stores: each of the two lands at a 32-byte stride, and the L2
+      // merges both halves of every line before it goes to HBM (non-temporal
+      // stores leave half-filled lines: 68 us instead of 39 us per call at
+      // 256 x 128256)
+      out_row[2 * vi] = f32x4{o[0], o[1], o[2], o[3]};
+      out_row[2 * vi + 1] = f32x4{o[4], o[5], o[6], o[7]};
     }
     return;
   }
