@@ -6,8 +6,10 @@
 //   K  top-k threshold: radix select on order keys, 8 bits per pass, then the
 //      lowest-index members of the boundary tie group by a radix select on the
 //      inverted index                                  (only rows with top-k)
-//   P  top-p cutoff: radix select on probability mass -- the largest key v with
-//      mass(key >= v) >= p * mass(K), 8 bits per pass  (only rows with top-p)
+//   P  top-p cutoff: the largest key v with mass(key >= v) >= p * mass(K).
+//      With k <= 1024, from K's members gathered in shared memory (each
+//      member's mass above it); otherwise a radix select on probability mass,
+//      8 bits per pass                                   (only rows with top-p)
 //   F  Philox noise and the perturbed argmax over P, plus the mass of P
 //
 // Probability masses are summed as 64-bit fixed-point integers, so every sum is
@@ -125,6 +127,10 @@ __device__ __forceinline__ int find_digit_desc(const C* hist, C base, Reach reac
   return d;
 }
 
+// Largest top-k whose members are gathered in shared memory for the top-p
+// cutoff (K has exactly k entries).
+constexpr int kKMax = 1024;
+
 struct Shared {
   uint32_t hist32[256];
   unsigned long long hist64[256];
@@ -132,6 +138,10 @@ struct Shared {
   int32_t widx[kWaves];
   unsigned long long wsum[kWaves];
   float wz[kWaves];
+  uint32_t kkey[kKMax];              // members of K: order keys ...
+  unsigned long long kmass[kKMax];   // ... and fixed-point masses
+  uint32_t nk;
+  uint32_t vcmin;
 };
 
 __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, Shared& sh) {
@@ -323,6 +333,42 @@ __device__ __forceinline__ void general_row(const RowArgs& a, int r, Shared& sh)
   if (p_on) {
     if (!(pq > 0.0f)) {
       vc = kmax;
+    } else if (k_on && (uint32_t)kq <= (uint32_t)kKMax) {
+      // K holds exactly k entries: gather their keys and masses, then each
+      // member's mass above it (strictly larger keys: whole tie groups) decides
+      // P directly -- j in P iff mass(K, key > key_j) < p * mass(K).  The
+      // smallest key in P is the cutoff; the sums are the same integers as
+      // the radix select's, so the cutoff is too.
+      if (tid == 0) {
+        sh.nk = 0;
+        sh.vcmin = 0xFFFFFFFFu;
+      }
+      __syncthreads();
+      for_groups(row, v, vec, [&](int64_t j0, const uint32_t* raw) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t k = Key::from_bits(raw[i]);
+          if (in_k(k, j0 + i)) {
+            const uint32_t slot = atomicAdd(&sh.nk, 1u);
+            if (slot < (uint32_t)kKMax) {
+              sh.kkey[slot] = k;
+              sh.kmass[slot] = fixed_mass(raw[i]);
+            }
+          }
+        }
+      });
+      __syncthreads();
+      const uint32_t nk = sh.nk < (uint32_t)kKMax ? sh.nk : (uint32_t)kKMax;
+      const unsigned long long zk = block_sum_u64((uint32_t)tid < nk ? sh.kmass[tid] : 0ull, sh);
+      const double target = (double)pq * (double)zk;
+      if ((uint32_t)tid < nk) {
+        const uint32_t kt = sh.kkey[tid];
+        unsigned long long above = 0;
+        for (uint32_t i = 0; i < nk; ++i) above += sh.kkey[i] > kt ? sh.kmass[i] : 0ull;
+        if ((double)above < target) atomicMin(&sh.vcmin, kt);
+      }
+      __syncthreads();
+      vc = sh.vcmin;
     } else {
       uint32_t prefix = 0, pmask = 0;
       unsigned long long above = 0, bin = 0;
