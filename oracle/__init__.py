@@ -26,7 +26,10 @@ reading taken is stated in the docstring of the function that takes it.
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against
 something other than itself (two independent Philox libraries, brute-force
 enumeration on tiny vocabularies, closed forms, chi-square frequency tests,
-scipy's log_softmax).  No function is "parity unpinned".
+scipy's log_softmax), except ``verify_chain`` (``oracle/verify.py``): the page
+names that step and its outputs but prints neither its arithmetic nor a value,
+so it is "parity unpinned" -- pinned only to hand-worked cases of the reading
+stated there and to invariants.
 """
 
 from .philox import philox4x32_10, noise_words, uniform_from_words, gumbel_from_uniform
@@ -46,10 +49,11 @@ from .sampler import (
     TOP_P_EPS,
     NEAR_TIE_REL,
 )
+from .verify import verify_chain
 
 __all__ = [
     "philox4x32_10", "noise_words", "uniform_from_words", "gumbel_from_uniform",
     "RowParams", "RowResult", "order_key_sort", "top_k_mask", "top_p_mask",
     "process_row", "sample_row", "sample", "raw_log_probs_at", "log_probs", "build_spec_map",
-    "GREEDY_T_MAX", "TOP_P_EPS", "NEAR_TIE_REL",
+    "GREEDY_T_MAX", "TOP_P_EPS", "NEAR_TIE_REL", "verify_chain",
 ]

@@ -313,3 +313,53 @@ def test_log_probs_at_token_ids_and_full_rows():
     samples = oracle.sample(logits, 5, params)
     for r, s in enumerate(samples):
         assert s.logprob == full[r, s.token]
+
+
+# ---------------------------------------------------------------------------
+# Chain verification of speculative drafts (TokenSpeed page, TritonSamplingBackend.verify).
+# Parity unpinned: the page prints neither the kernel's steps nor a value; the
+# pins are hand-worked cases of the stated reading and invariants.
+
+def test_verify_chain_golden_cases():
+    with open(os.path.join(HERE, "golden", "verify_chain.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        pred, idx, acc = oracle.verify_chain(np.array(c["candidates"]), np.array(c["target"]))
+        assert pred.tolist() == c["predicts"], c
+        assert idx.tolist() == c["accept_index"], c
+        assert acc.tolist() == c["accept_length"], c
+
+
+def test_verify_chain_invariants():
+    rng = np.random.default_rng(5)
+    for n in (1, 2, 4, 7):
+        bs = 50
+        cand = rng.integers(0, 3, size=(bs, n))
+        tgt = rng.integers(0, 3, size=bs * n)
+        pred, idx, acc = oracle.verify_chain(cand, tgt)
+        for b in range(bs):
+            a = int(acc[b])
+            assert 0 <= a <= n - 1
+            # every accepted draft equals the target sample before it, and the
+            # first rejected one does not
+            for i in range(a):
+                assert cand[b, i + 1] == tgt[b * n + i]
+            if a < n - 1:
+                assert cand[b, a + 1] != tgt[b * n + a]
+            assert idx[b].tolist() == [b * n + i for i in range(a + 1)] + [-1] * (n - 1 - a)
+            assert pred[b * n:(b + 1) * n].tolist() == tgt[b * n:b * n + a + 1].tolist() + [-1] * (n - 1 - a)
+
+
+def test_verify_chain_accepts_everything_when_drafts_are_the_target_samples():
+    # drafts taken from the target samples themselves (shifted by one) are all
+    # accepted: the chain emits every target sample
+    rng = np.random.default_rng(9)
+    bs, n = 8, 5
+    tgt = rng.integers(0, 1000, size=bs * n)
+    cand = np.empty((bs, n), dtype=np.int64)
+    cand[:, 0] = rng.integers(0, 1000, size=bs)
+    cand[:, 1:] = tgt.reshape(bs, n)[:, :-1]
+    pred, idx, acc = oracle.verify_chain(cand, tgt)
+    assert np.all(acc == n - 1)
+    assert np.array_equal(pred, tgt)
+    assert np.array_equal(idx.reshape(-1), np.arange(bs * n))
