@@ -103,6 +103,44 @@ def cpu_baseline(wl, budget_s: float, call: str = "sample"):
                       f"one process ({dt:.1f} s)"}
 
 
+def verify_inputs(wl, sampler, logits, params, gather, req, dev):
+    """Chain-verification inputs on the speculative workload: the decode
+    requests (those owning 1 + S rows, first in the layout) with one sampled
+    target token per row, and seeded draft chains that follow those samples for
+    a random number of steps before diverging."""
+    counts = np.bincount(wl.token_to_request_index.numpy())
+    n = int(counts.max())
+    bs = int(np.sum(counts == n))
+    ids, _ = sampler.sample(logits, wl.n, params, no_top_k=wl.no_top_k, no_top_p=wl.no_top_p,
+                            gather_indices=gather, token_to_request_index=req,
+                            return_logprobs=True)
+    tgt = ids[:bs * n].contiguous()
+    t = tgt.cpu().numpy().reshape(bs, n)
+    rng = np.random.default_rng(17)
+    cand = rng.integers(0, wl.vocab, size=(bs, n)).astype(np.int32)
+    stop = rng.integers(0, n, size=bs)
+    for b in range(bs):
+        cand[b, 1:stop[b] + 1] = t[b, :stop[b]]
+    return {"bs": bs, "n": n, "tgt": tgt, "cand": torch.from_numpy(cand.reshape(-1)).to(dev)}
+
+
+def verify_cpu_baseline(verify, budget_s: float):
+    """The oracle's chain verification on the same requests, repeated for the budget."""
+    import oracle
+    cand = verify["cand"].cpu().numpy().reshape(verify["bs"], verify["n"])
+    tgt = verify["tgt"].cpu().numpy()
+    t0 = time.perf_counter()
+    reps = 0
+    while reps < 1 or (time.perf_counter() - t0 < min(budget_s, 2.0) and reps < 1000):
+        oracle.verify_chain(cand, tgt)
+        reps += 1
+    dt = time.perf_counter() - t0
+    rows = verify["bs"] * verify["n"]
+    return {"value": rows * reps / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} passes over the {verify['bs']} decode requests, python loops, "
+                      f"one process ({dt:.2f} s)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,9 +148,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="joint_128k", choices=sorted(synth.WORKLOAD_IDS))
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: auto)")
-    ap.add_argument("--call", default="sample", choices=("sample", "log_probs", "raw_log_probs"),
-                    help="time ts_sample (default), ts_log_probs with full [n, V] rows, or "
-                         "ts_raw_log_probs_at at the sampled ids")
+    ap.add_argument("--call", default="sample",
+                    choices=("sample", "log_probs", "raw_log_probs", "verify_chain"),
+                    help="time ts_sample (default), ts_log_probs with full [n, V] rows, "
+                         "ts_raw_log_probs_at at the sampled ids, or ts_verify_chain over the "
+                         "decode requests of the speculative workload (spec_mix)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -213,6 +253,34 @@ def main():
             if st != tsa.TS_OK:
                 raise RuntimeError(f"ts_raw_log_probs_at failed with status {st}")
 
+    verify = None
+    if args.call == "verify_chain":
+        if wl.token_to_request_index is None:
+            print("--call verify_chain needs the speculative workload (--workload spec_mix)",
+                  file=sys.stderr)
+            sys.exit(2)
+        verify = verify_inputs(wl, sampler, logits[0], params, gather, req, dev)
+        vb, vn, cand, tgt = verify["bs"], verify["n"], verify["cand"], verify["tgt"]
+        pred = torch.empty(vb * vn, dtype=torch.int32, device=dev)
+        aidx = torch.empty(vb * vn, dtype=torch.int32, device=dev)
+        alen = torch.empty(vb, dtype=torch.int32, device=dev)
+
+        def step_checked(i):
+            tsa.verify_chain(cand.view(vb, vn), tgt, predicts=pred, accept_index=aidx.view(vb, vn),
+                             accept_length=alen)
+
+        v_args = [vb, vn, ctypes.c_void_p(cand.data_ptr()), ctypes.c_void_p(tgt.data_ptr()),
+                  ctypes.c_void_p(pred.data_ptr()), ctypes.c_void_p(aidx.data_ptr()),
+                  ctypes.c_void_p(alen.data_ptr()), stream_ptr]
+        ts_verify = lib.ts_verify_chain
+
+        def step(i):
+            st = ts_verify(*v_args)
+            if st != tsa.TS_OK:
+                raise RuntimeError(f"ts_verify_chain failed with status {st}")
+
+        nbytes = vb * (16 * vn + 4)
+
     if args.copy_probe_mb:
         a = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -237,8 +305,9 @@ def main():
     wall = time.perf_counter() - t0
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
 
-    rows_per_s = wl.n * args.steps / wall
-    gbps = logits_bytes(wl) * args.steps / wall / 1e9
+    rows = wl.n if verify is None else verify["bs"] * verify["n"]
+    rows_per_s = rows * args.steps / wall
+    gbps = (logits_bytes(wl) if verify is None else 0) * args.steps / wall / 1e9
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     out = {
         "metric": METRIC,
@@ -256,7 +325,7 @@ def main():
         "logits_read_gbps": gbps,
         "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
         "config": {"workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}",
-                   "rows": wl.n, "vocab": wl.vocab, "logits_dtype": str(wl.logits.dtype).split(".")[-1],
+                   "rows": rows, "vocab": wl.vocab, "logits_dtype": str(wl.logits.dtype).split(".")[-1],
                    "route": ["none", "top-k", "top-p", "joint"][tsa.select_route(wl.no_top_k, wl.no_top_p)],
                    "call": args.call,
                    "input_copies": copies, "logits_bytes_per_step": logits_bytes(wl),
@@ -266,8 +335,13 @@ def main():
                      "traffic": measured_traffic(args.workload) if args.call == "sample" else None,
                      "kernel_ms_per_launch": kernel_ms},
     }
+    if verify is not None:
+        out["config"]["verify"] = {"requests": verify["bs"], "rows_per_request": verify["n"],
+                                   "mean_accepted_drafts": float(alen.float().mean().item())}
+        out["roofline"]["bound"] = "launch"
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, args.call)
+        out["cpu_baseline"] = (verify_cpu_baseline(verify, args.cpu_budget) if verify is not None
+                               else cpu_baseline(wl, args.cpu_budget, args.call))
     print(json.dumps(out), flush=True)
 
 

@@ -189,6 +189,32 @@ ts_status ts_build_spec_map(int32_t num_decode, int32_t num_prefill, int32_t num
                             int32_t* out_map, int32_t capacity, int32_t on_device,
                             void* stream, int32_t* out_n);
 
+/* Chain verification of speculative drafts against the target's samples (the
+ * verify step of the TokenSpeed Triton sampling backend page,
+ * TritonSamplingBackend.verify: one target sample per row of the speculative
+ * layout, then each request's draft chain is checked against them; the page
+ * names the step and its outputs but not its arithmetic, so this is a reading).
+ * Request b in [0, bs) owns rows b*n_per_req .. b*n_per_req + n_per_req - 1.
+ *   candidates      device int32 [bs, n_per_req] row-major: column 0 the
+ *                   request's last verified token, columns 1.. its drafts
+ *   target_sampled  device int32 [bs * n_per_req]: the target's sample per row
+ *                   (e.g. ts_sample's out_ids over the decode rows)
+ *   predicts        device int32 [bs * n_per_req], written
+ *   accept_index    device int32 [bs * n_per_req] ([bs, n_per_req]), written
+ *   accept_length   device int32 [bs], written
+ * Draft i+1 of request b is accepted while every earlier draft was and it
+ * equals target_sampled[b*n_per_req + i]; accept_length[b] counts the accepted
+ * drafts (0 .. n_per_req-1), so a request emits accept_length[b] + 1 tokens.
+ * Positions i = 0 .. accept_length[b] get predicts = target_sampled[b*n+i] and
+ * accept_index = b*n + i; every other position gets -1 in both.  Buffers are
+ * caller-owned and must not overlap; the call is enqueued on `stream`
+ * (hipStream_t) and needs no handle and no workspace.
+ * Errors: TS_E_ARG (bs < 0, n_per_req < 1, a NULL pointer with bs > 0),
+ * TS_E_SIZE (bs * n_per_req > 2^31 - 1), TS_E_HIP. */
+ts_status ts_verify_chain(int32_t bs, int32_t n_per_req, const int32_t* candidates,
+                          const int32_t* target_sampled, int32_t* predicts,
+                          int32_t* accept_index, int32_t* accept_length, void* stream);
+
 /* The route the flags select (pure host function, no GPU). */
 ts_route ts_select_route(int32_t no_top_k, int32_t no_top_p);
 

@@ -133,3 +133,15 @@ def test_raw_log_probs_argument_checks_on_validation_handle(lib):
                                        None) == tsa.TS_E_ARG
     finally:
         lib.ts_destroy(h)
+
+
+def test_verify_chain_argument_checks(lib):
+    # error paths and the empty batch return before any GPU call
+    assert lib.ts_verify_chain(0, 4, None, None, None, None, None, None) == tsa.TS_OK
+    assert lib.ts_verify_chain(-1, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None) == tsa.TS_E_ARG
+    assert lib.ts_verify_chain(2, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == tsa.TS_E_ARG
+    assert lib.ts_verify_chain(1 << 20, 1 << 12, FAKE, FAKE, FAKE, FAKE, FAKE, None) == tsa.TS_E_SIZE
+    for k in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[k] = None
+        assert lib.ts_verify_chain(2, 4, *ptrs, None) == tsa.TS_E_ARG

@@ -417,3 +417,60 @@ def test_log_probs_with_more_rows_than_cus():
     print(f"[case] log_probs mixed rows={wl.n} vocab={wl.vocab}", flush=True)
     gpu = parity.gpu_log_probs(wl)
     parity.compare_log_probs(gpu, parity.oracle_log_probs(wl), parity.oracle_sample(wl)).check()
+
+
+def _draft_chains(bs, n, rng, target):
+    """Drafts that follow the target samples for a random number of steps, then
+    diverge (a draft that equals the target by chance is accepted too)."""
+    tgt = target.reshape(bs, n)
+    cand = rng.integers(0, 50, size=(bs, n)).astype(np.int32)
+    stop = rng.integers(0, n, size=bs)             # drafts copied before this position
+    for b in range(bs):
+        for i in range(1, n):
+            if i <= stop[b]:
+                cand[b, i] = tgt[b, i - 1]
+    return cand
+
+
+@pytest.mark.parametrize("bs,n", [(1, 1), (5, 2), (64, 4), (300, 8), (2048, 3)])
+def test_verify_chain_matches_oracle(bs, n):
+    rng = np.random.default_rng(bs * 31 + n)
+    target = rng.integers(0, 50, size=bs * n).astype(np.int32)
+    cand = _draft_chains(bs, n, rng, target)
+    print(f"[case] verify_chain bs={bs} n={n}", flush=True)
+    pred, idx, acc = tsa.verify_chain(torch.from_numpy(cand).cuda(), torch.from_numpy(target).cuda())
+    torch.cuda.synchronize()
+    want_p, want_i, want_a = oracle.verify_chain(cand, target)
+    assert np.array_equal(pred.cpu().numpy(), want_p)
+    assert np.array_equal(idx.cpu().numpy(), want_i)
+    assert np.array_equal(acc.cpu().numpy(), want_a)
+
+
+def test_verify_chain_on_sampled_speculative_rows():
+    """The speculative layout end to end: sample the decode rows of the mixed
+    workload, draft chains that follow those samples part of the way, verify;
+    int64 inputs are converted, and an empty batch is a no-op."""
+    wl = synth.make("spec_mix", rows=24, vocab=16384)
+    ids, lps = parity.gpu_sample(wl)
+    ref = parity.oracle_sample(wl)
+    parity.compare_samples(ids, lps, ref).check()
+    n = 4                                           # 1 + 3 rows per decode request
+    bs = int(np.sum(np.bincount(wl.token_to_request_index.numpy()) == n))   # decode requests
+    rows = bs * n                                   # the decode rows come first
+    rng = np.random.default_rng(3)
+    target = ids[:rows].astype(np.int32)
+    cand = _draft_chains(bs, n, rng, target)
+    print(f"[case] verify_chain on sampled rows bs={bs}", flush=True)
+    pred, idx, acc = tsa.verify_chain(torch.from_numpy(cand.astype(np.int64)).cuda(),
+                                      torch.from_numpy(target.astype(np.int64)).cuda())
+    torch.cuda.synchronize()
+    # against the oracle's own samples where no row is a flagged near tie
+    # (those are counted by compare_samples above and may differ by design)
+    if not any(r.flagged for r in ref[:rows]):
+        want_p, want_i, want_a = oracle.verify_chain(cand, np.array([r.token for r in ref[:rows]]))
+        assert np.array_equal(pred.cpu().numpy(), want_p)
+        assert np.array_equal(idx.cpu().numpy(), want_i)
+        assert np.array_equal(acc.cpu().numpy(), want_a)
+    e = tsa.verify_chain(torch.empty((0, 4), dtype=torch.int32, device="cuda"),
+                         torch.empty(0, dtype=torch.int32, device="cuda"))
+    assert e[0].numel() == 0 and e[2].numel() == 0

@@ -67,11 +67,12 @@ def library() -> ctypes.CDLL:
                                         c_vp, c_vp]
     lib.ts_build_spec_map.argtypes = [c_i32, c_i32, c_i32, c_vp, c_i32, c_i32, c_vp,
                                       ctypes.POINTER(c_i32)]
+    lib.ts_verify_chain.argtypes = [c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
     lib.ts_select_route.argtypes = [c_i32, c_i32]
     lib.ts_status_str.argtypes = [c_i32]
     lib.ts_status_str.restype = ctypes.c_char_p
     for name in ("ts_create", "ts_destroy", "ts_sample", "ts_log_probs", "ts_raw_log_probs_at",
-                 "ts_build_spec_map", "ts_select_route"):
+                 "ts_build_spec_map", "ts_verify_chain", "ts_select_route"):
         getattr(lib, name).restype = ctypes.c_int32
     _lib = lib
     return lib
@@ -279,4 +280,38 @@ def build_spec_map(num_decode: int, num_prefill: int, num_spec: int, device=None
     return out, int(got.value)
 
 
-__all__ = ["Sampler", "SamplingParams", "build_spec_map", "select_route", "library", "LIB_PATH"]
+def verify_chain(candidates: torch.Tensor, target_sampled: torch.Tensor, *,
+                 predicts: Optional[torch.Tensor] = None,
+                 accept_index: Optional[torch.Tensor] = None,
+                 accept_length: Optional[torch.Tensor] = None):
+    """(predicts [bs * N], accept_index [bs, N], accept_length [bs]) for the
+    draft chains ``candidates`` [bs, N] (column 0 the last verified token) against
+    the target samples ``target_sampled`` [bs * N], on their device and current
+    stream.  A request emits accept_length + 1 tokens (ts_verify_chain)."""
+    if candidates.dim() != 2:
+        raise ValueError("candidates must be [bs, N]")
+    bs, n = int(candidates.shape[0]), int(candidates.shape[1])
+    dev = candidates.device
+    if dev.type != "cuda":
+        raise ValueError("candidates must be on a GPU")
+    cand = _index_i32(candidates.reshape(-1).contiguous(), "candidates", bs * n, dev)
+    tgt = _index_i32(target_sampled.reshape(-1).contiguous(), "target_sampled", bs * n, dev)
+
+    def _out(t, shape, name):
+        if t is None:
+            return torch.empty(shape, dtype=torch.int32, device=dev)
+        if t.dtype != torch.int32 or tuple(t.shape) != shape or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name} must be a contiguous int32 tensor of shape {shape} on {dev}")
+        return t
+
+    predicts = _out(predicts, (bs * n,), "predicts")
+    accept_index = _out(accept_index, (bs, n), "accept_index")
+    accept_length = _out(accept_length, (bs,), "accept_length")
+    _check(library().ts_verify_chain(bs, n, _ptr(cand), _ptr(tgt), _ptr(predicts),
+                                     _ptr(accept_index), _ptr(accept_length), _stream(dev)),
+           "ts_verify_chain")
+    return predicts, accept_index, accept_length
+
+
+__all__ = ["Sampler", "SamplingParams", "build_spec_map", "verify_chain", "select_route",
+           "library", "LIB_PATH"]

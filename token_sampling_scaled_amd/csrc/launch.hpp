@@ -90,4 +90,9 @@ hipError_t launch_rows_general(const RowArgs& a, DType dtype, Route route, OutMo
 hipError_t launch_spec_map(int32_t num_decode, int32_t num_prefill, int32_t num_spec,
                            int32_t* out_map, hipStream_t stream);
 
+// Chain verification of speculative drafts (one thread per request).
+hipError_t launch_verify_chain(int32_t bs, int32_t n, const int32_t* candidates,
+                               const int32_t* target_sampled, int32_t* predicts,
+                               int32_t* accept_index, int32_t* accept_length, hipStream_t stream);
+
 }  // namespace tss

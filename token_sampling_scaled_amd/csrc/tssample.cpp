@@ -293,4 +293,19 @@ ts_status ts_build_spec_map(int32_t num_decode, int32_t num_prefill, int32_t num
              : TS_E_HIP;
 }
 
+ts_status ts_verify_chain(int32_t bs, int32_t n_per_req, const int32_t* candidates,
+                          const int32_t* target_sampled, int32_t* predicts, int32_t* accept_index,
+                          int32_t* accept_length, void* stream) {
+  if (bs < 0 || n_per_req < 1) return TS_E_ARG;
+  if ((int64_t)bs * n_per_req > 0x7FFFFFFF) return TS_E_SIZE;
+  if (bs == 0) return TS_OK;
+  if (candidates == nullptr || target_sampled == nullptr || predicts == nullptr ||
+      accept_index == nullptr || accept_length == nullptr)
+    return TS_E_ARG;
+  return tss::launch_verify_chain(bs, n_per_req, candidates, target_sampled, predicts, accept_index,
+                                  accept_length, (hipStream_t)stream) == hipSuccess
+             ? TS_OK
+             : TS_E_HIP;
+}
+
 }  // extern "C"
