@@ -138,8 +138,8 @@ struct Shared {
   int32_t widx[kWaves];
   unsigned long long wsum[kWaves];
   float wz[kWaves];
-  uint32_t kkey[kKMax];              // members of K: order keys ...
-  unsigned long long kmass[kKMax];   // ... and fixed-point masses
+  alignas(16) uint32_t kkey[kKMax];              // members of K: order keys ...
+  alignas(16) unsigned long long kmass[kKMax];   // ... and fixed-point masses
   uint32_t nk;
   uint32_t vcmin;
 };
@@ -362,9 +362,20 @@ __device__ __forceinline__ void general_row(const RowArgs& a, int r, Shared& sh)
       const unsigned long long zk = block_sum_u64((uint32_t)tid < nk ? sh.kmass[tid] : 0ull, sh);
       const double target = (double)pq * (double)zk;
       if ((uint32_t)tid < nk) {
+        // four members per 16-byte key read, several reads in flight (one
+        // shared-memory read per iteration would wait out its latency each time)
+        const uint4* k4 = reinterpret_cast<const uint4*>(sh.kkey);
+        const ulonglong2* m2 = reinterpret_cast<const ulonglong2*>(sh.kmass);
         const uint32_t kt = sh.kkey[tid];
         unsigned long long above = 0;
-        for (uint32_t i = 0; i < nk; ++i) above += sh.kkey[i] > kt ? sh.kmass[i] : 0ull;
+#pragma unroll 4
+        for (uint32_t i = 0; i < nk; i += 4) {
+          const uint4 kk = k4[i >> 2];
+          const ulonglong2 ma = m2[i >> 1];
+          const ulonglong2 mb = m2[(i >> 1) + 1];
+          above += (kk.x > kt ? ma.x : 0ull) + (i + 1 < nk && kk.y > kt ? ma.y : 0ull) +
+                   (i + 2 < nk && kk.z > kt ? mb.x : 0ull) + (i + 3 < nk && kk.w > kt ? mb.y : 0ull);
+        }
         if ((double)above < target) atomicMin(&sh.vcmin, kt);
       }
       __syncthreads();
