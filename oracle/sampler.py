@@ -15,9 +15,14 @@ Per output row r (all arithmetic in fp64, one row at a time, no blocking):
    Reading: k is active when 1 <= k < V; K is the first min(k, #finite) indices
    in the order (x descending, index ascending) on the raw logits.  Temperature
    is a positive scale, so it cannot change this set.
-4. Temperature: s = x / T.  Reading: T < GREEDY_T_MAX means greedy (the
-   TokenSpeed page routes all-greedy batches to an argmax); the greedy pick is
-   the first index in the order of step 3 and its log-prob is 0 (a point mass).
+4. Temperature: s = x / T.  Reading: a temperature below GREEDY_T_MAX means
+   greedy (the TokenSpeed page routes all-greedy batches to an argmax); the
+   greedy pick is the first index in the order of step 3 and its log-prob is 0
+   (a point mass).  Parameters arrive as fp32 values, and both thresholds
+   (GREEDY_T_MAX here, 1 - TOP_P_EPS in step 5) are compared in fp32: a row is
+   greedy unless fp32(T) >= fp32(1e-5), and top-p is on only when
+   fp32(p) < fp32(1) - fp32(1e-6) (an fp32 subtraction), so a parameter that
+   equals a threshold falls on the same side for every implementation.
 5. Top-p on the top-k distribution (joint filtering, top-k first; reading of
    "top-k / top-p sampling distribution" in ``log_probs_kernel``).  With
    pi = softmax(s) over K, index j is kept when the mass of the members of K
@@ -66,6 +71,9 @@ class Outcome:
     token: int
     logprob: float
     keep: np.ndarray  # bool [V], the set P this outcome samples from
+    # float64 [V]: log-probs of the processed distribution over ``keep`` (set for
+    # the alternatives of a top-p near tie, whose kept set differs from the row's)
+    lp_row: Optional[np.ndarray] = None
 
 
 @dataclass
@@ -82,6 +90,16 @@ class RowResult:
     @property
     def flagged(self) -> bool:
         return self.flag_sample or self.flag_topp
+
+
+def is_greedy(t: float) -> bool:
+    """Greedy unless fp32(t) >= fp32(GREEDY_T_MAX) (a NaN temperature is greedy too)."""
+    return not (np.float32(t) >= np.float32(GREEDY_T_MAX))
+
+
+def top_p_active(p: float) -> bool:
+    """Top-p filters only when fp32(p) < fp32(1) - fp32(TOP_P_EPS), evaluated in fp32."""
+    return bool(np.float32(p) < np.float32(1.0) - np.float32(TOP_P_EPS))
 
 
 def canonical_logits(x) -> np.ndarray:
@@ -133,7 +151,7 @@ def top_p_mask(x: np.ndarray, s: np.ndarray, topk: np.ndarray, p: float):
     w = np.exp(s - m)
     z = np.sum(w[topk])
     cum = np.cumsum([np.sum(w[g]) for g in groups]) / z
-    if p >= 1.0 - TOP_P_EPS:
+    if not top_p_active(p):
         kept = len(groups)
     else:
         before = np.concatenate(([0.0], cum[:-1]))
@@ -175,7 +193,7 @@ def process_row(x, params: RowParams, use_top_k: bool = True, use_top_p: bool = 
     if not topk.any():
         return dict(x=x, s=None, topk=topk, keep=topk, groups=[], cum=np.zeros(0), kept=0,
                     lp_row=np.full(v, np.nan), greedy=False)
-    if t < GREEDY_T_MAX:
+    if is_greedy(t):
         keep = np.zeros(v, dtype=bool)
         keep[order_key_sort(x)[0]] = True
         lp_row = np.where(keep, 0.0, -np.inf)
@@ -206,7 +224,7 @@ def sample_row(x, params: RowParams, r: int, step_offset: int = 0,
     # Top-p near ties: the last kept group may be dropped, or the next one kept.
     p = float(params.top_p) if use_top_p else 1.0
     groups, cum, kept = d["groups"], d["cum"], d["kept"]
-    if p < 1.0 - TOP_P_EPS and groups:
+    if top_p_active(p) and groups:
         alt_sets = []
         if kept >= 2 and abs(cum[kept - 2] - p) <= NEAR_TIE_REL * p:
             a = keep.copy()
@@ -221,7 +239,7 @@ def sample_row(x, params: RowParams, r: int, step_offset: int = 0,
             lp_a = _lp_row(s, a)
             t_a, near_a = _draw(s, a, params.seed, r, step_offset)
             for alt in near_a:
-                res.alternatives.append(Outcome(int(alt), float(lp_a[alt]), a))
+                res.alternatives.append(Outcome(int(alt), float(lp_a[alt]), a, lp_a))
     return res
 
 

@@ -271,6 +271,91 @@ def test_near_tie_is_flagged_with_both_alternatives():
     assert r.flag_sample and {o.token for o in r.alternatives} == {1, 4}
 
 
+# Rows with exactly known softmax masses for the top-p near-tie pins: logits
+# x = T ln(w), so s = x / T = ln(w) and pi = w / sum(w).  Tie groups (in
+# descending logit order): {0} 0.3, {1, 2} 0.4, {3, 4, 5} 0.3, so the
+# cumulative masses through each group are 0.3, 0.7 and 1.0.
+_TP_W = np.array([0.3, 0.2, 0.2, 0.1, 0.1, 0.1])
+_TP_ALL, _TP_01, _TP_0 = {0, 1, 2, 3, 4, 5}, {0, 1, 2}, {0}
+
+
+def _tp_expect_lp(members):
+    w = np.where(np.isin(np.arange(6), sorted(members)), _TP_W, 0.0)
+    with np.errstate(divide="ignore"):
+        return np.where(w > 0, np.log(w / w.sum()), -np.inf)
+
+
+def _tp_expect_token(members, seed, r, off):
+    """Brute force: argmax over the set of ln(w) + g (lowest index on ties)."""
+    g = philox.gumbel_from_uniform(philox.uniform_from_words(philox.noise_words(seed, r, off, np.arange(6))))
+    return max(sorted(members), key=lambda j: (math.log(_TP_W[j]) + g[j], -j))
+
+
+@pytest.mark.parametrize("t", [1.0, 0.7])
+@pytest.mark.parametrize("p,kept,alts", [
+    (0.7 * (1 + 4e-6), _TP_ALL, [_TP_01]),   # just above C(1) = 0.7: group 2 kept, may drop
+    (0.7 * (1 - 4e-6), _TP_01, [_TP_ALL]),   # just below C(1): group 2 dropped, may be kept
+    (0.3 * (1 + 4e-6), _TP_01, [_TP_0]),     # just above C(0) = 0.3: group 1 kept, may drop
+    (0.3 * (1 - 4e-6), _TP_0, [_TP_01]),     # just below C(0): group 1 dropped, may be kept
+    (0.7 * (1 + 3e-5), _TP_ALL, []),         # outside the 1e-5 * p band: not flagged
+    (0.7 * (1 - 3e-5), _TP_01, []),
+    (0.3 * (1 + 3e-5), _TP_01, []),
+])
+def test_top_p_near_tie_flag_and_alternative_sets(t, p, kept, alts):
+    """Top-p near ties: a cumulative tie-group mass within 1e-5 * p of p flags
+    the row, and the listed alternatives sample from exactly the set with that
+    boundary group toggled (whole tie groups), with that set's log-probs."""
+    x = t * np.log(_TP_W)
+    for seed in (3, 8, 21):
+        r = oracle.sample_row(x, RowParams(t, 0, p, seed), 2, 5)
+        assert set(np.nonzero(r.keep)[0]) == kept
+        assert r.token == _tp_expect_token(kept, seed, 2, 5)
+        assert np.allclose(r.lp_row, _tp_expect_lp(kept), rtol=0, atol=1e-12)
+        assert r.flag_topp == bool(alts)
+        topp_alts = [o for o in r.alternatives if o.lp_row is not None]
+        assert sorted({tuple(np.nonzero(o.keep)[0]) for o in topp_alts}) == \
+            sorted(tuple(sorted(a)) for a in alts)
+        for o in topp_alts:
+            members = set(np.nonzero(o.keep)[0])
+            assert o.token == _tp_expect_token(members, seed, 2, 5)
+            assert np.allclose(o.lp_row, _tp_expect_lp(members), rtol=0, atol=1e-12)
+            assert abs(o.logprob - o.lp_row[o.token]) < 1e-15
+
+
+def test_top_p_near_tie_inside_top_k():
+    """Joint: with k = 4 the top-k set cuts the group {3, 4, 5} at index 3, and
+    the renormalised K-masses are 0.375, 0.5, 0.125 (cumulative 0.375, 0.875,
+    1).  A p just above 0.875 keeps index 3 and lists the set without it."""
+    x = np.log(_TP_W)
+    r = oracle.sample_row(x, RowParams(1.0, 4, 0.875 * (1 + 4e-6), 9), 0, 0)
+    assert set(np.nonzero(r.topk)[0]) == {0, 1, 2, 3}
+    assert set(np.nonzero(r.keep)[0]) == {0, 1, 2, 3} and r.flag_topp
+    alt = [o for o in r.alternatives if o.lp_row is not None]
+    assert {tuple(np.nonzero(o.keep)[0]) for o in alt} == {(0, 1, 2)}
+    assert np.allclose(alt[0].lp_row[:3], np.log(np.array([0.3, 0.2, 0.2]) / 0.7), rtol=0, atol=1e-12)
+    r = oracle.sample_row(x, RowParams(1.0, 4, 0.875 * (1 + 3e-5), 9), 0, 0)
+    assert not r.flag_topp
+
+
+def test_thresholds_are_compared_in_fp32():
+    """A temperature equal to fp32(1e-5) samples and anything below it is
+    greedy; a top-p equal to fp32(1) - fp32(1e-6) (= fp32(0.999999)) is off and
+    the next fp32 value below it filters."""
+    t_thr = float(np.float32(1e-5))
+    assert not oracle.sampler.is_greedy(t_thr)
+    assert oracle.sampler.is_greedy(float(np.nextafter(np.float32(t_thr), np.float32(0))))
+    assert oracle.sampler.is_greedy(float("nan")) and oracle.sampler.is_greedy(0.0)
+    p_thr = float(np.float32(1.0) - np.float32(1e-6))
+    assert p_thr == float(np.float32(0.999999))
+    assert not oracle.sampler.top_p_active(p_thr)
+    assert oracle.sampler.top_p_active(float(np.nextafter(np.float32(p_thr), np.float32(0))))
+    assert not oracle.sampler.top_p_active(float("nan"))
+    # end to end: at the temperature threshold the row is sampled, not greedy
+    x = np.array([2.0, 2.0, 1.0])
+    r = oracle.sample_row(x, RowParams(t_thr, 0, 1.0, 4), 0, 0)
+    assert r.keep.sum() == 3
+
+
 def test_gather_map_and_spec_layout():
     rng = np.random.default_rng(2)
     logits = rng.normal(0, 2, size=(12, 64))
