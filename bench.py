@@ -10,7 +10,9 @@ Infinity Cache, so each step reads its logits from HBM.
 
 Prints one JSON line: rows/s (value), logits-read GB/s, % of the 8 TB/s HBM
 peak, the roofline record of the sampling kernel (HIP events on the launch
-stream) and the CPU oracle's rate on a bounded sample of the same rows.
+stream) with the measured read ceiling of its launch shape, the CPU oracle's
+rate over a process pool, and the parity of the last timed step's output
+against that oracle (every row; near ties counted).
 """
 from __future__ import annotations
 
@@ -76,31 +78,99 @@ def measured_traffic(workload: str):
     return None
 
 
-def cpu_baseline(wl, budget_s: float, call: str = "sample"):
-    """The fp64 oracle, single process, on the leading rows of the same workload."""
+def cpu_baseline_and_parity(wl, budget_s: float, call: str, gpu_out, step_offset: int,
+                            token_ids=None):
+    """The fp64 oracle over a pool of host processes (oracle.parallel), on the
+    rows of the last timed step.  Its first pass computes every row of that
+    step and is compared with the GPU's output of that step (the parity
+    record); further passes over all rows at other step offsets run until
+    about ``budget_s`` seconds of CPU work are done, and the rate over every
+    pass is the baseline."""
     import oracle
+    from oracle.parallel import Pool, host_cores
+    from tests import parity
     x = wl.logits_f64()
     params = wl.params_numpy()
     gather = None if wl.gather_indices is None else wl.gather_indices.numpy()
     req = None if wl.token_to_request_index is None else wl.token_to_request_index.numpy()
-    t0 = time.perf_counter()
-    done = 0
-    while done < wl.n and time.perf_counter() - t0 < budget_s:
+    kw = dict(gather_indices=gather, token_to_request_index=req, no_top_k=wl.no_top_k,
+              no_top_p=wl.no_top_p)
+    with Pool() as pool:
+        pool.warm()
+        workers = pool.workers
+
+        def one_pass(off):
+            if call == "sample":
+                return pool.run("sample", x, wl.n, params, step_offset=off, light=True, **kw)
+            if call == "raw_log_probs":
+                return oracle.raw_log_probs_at(x, wl.n, token_ids, gather_indices=gather)
+            return pool.run("log_probs", x, wl.n, params, **kw)
+
+        t0 = time.perf_counter()
+        first = one_pass(step_offset)
+        passes = 1
+        while (time.perf_counter() - t0) * workers < budget_s and passes < 64:
+            one_pass(step_offset + passes)
+            passes += 1
+        dt = time.perf_counter() - t0
         if call == "sample":
-            oracle.sample(x, wl.n, params, gather_indices=gather, token_to_request_index=req,
-                          step_offset=wl.step_offset, no_top_k=wl.no_top_k, no_top_p=wl.no_top_p,
-                          rows=[done])
+            res = first
+            rep = parity.compare_samples(gpu_out[0], gpu_out[1], res)
         elif call == "raw_log_probs":
-            oracle.raw_log_probs_at(x, wl.n, np.zeros(wl.n, dtype=np.int32),
-                                    gather_indices=gather, rows=[done])
+            got, want = gpu_out, first
+            ok = (np.array_equal(np.isnan(got), np.isnan(want))
+                  and np.array_equal(np.isneginf(got), np.isneginf(want)))
+            fin = np.isfinite(want)
+            ok = ok and float(np.max(np.abs(got[fin] - want[fin]), initial=0.0)) <= parity.LP_ATOL
+            rep = parity.Report(rows=wl.n, mismatches=[] if ok else ["raw log-probs differ"])
         else:
-            oracle.log_probs(x, wl.n, params, gather_indices=gather, token_to_request_index=req,
-                             no_top_k=wl.no_top_k, no_top_p=wl.no_top_p, rows=[done])
-        done += 1
-    dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {done} of {wl.n} rows of the same workload, fp64 numpy, "
-                      f"one process ({dt:.1f} s)"}
+            res = pool.run("sample", x, wl.n, params, step_offset=step_offset, light=True, **kw)
+            rep = parity.compare_log_probs(gpu_out, first, res)
+    how = "one process" if call == "raw_log_probs" else f"{workers} worker processes"
+    base = {"value": wl.n * passes / dt, "unit": "rows/s",
+            "cores": 1 if call == "raw_log_probs" else workers, "host_cores": host_cores(),
+            "kind": "oracle",
+            "sample": f"{passes} pass(es) over all {wl.n} rows of the same workload (the first at "
+                      f"the last timed step's offset), fp64 numpy, {how} ({dt:.1f} s)"}
+    par = {"step_offset": step_offset, "rows": rep.rows, "flagged": rep.flagged,
+           "took_alternative": rep.diverged_flagged, "mismatches": len(rep.mismatches)}
+    if rep.mismatches:
+        par["first_mismatches"] = rep.mismatches[:3]
+    return base, par
+
+
+def read_ceiling(wl, logits, steps: int, warmup: int):
+    """The read-ceiling probe: the same logits bytes read with the sampling
+    kernel's launch shape (1024 threads per row, 16-byte loads), timed with
+    HIP events over the same rotating copies.  None when a row does not fit
+    that shape (more than 16 loads per thread)."""
+    from token_sampling_scaled_amd import probes
+    row_bytes = wl.vocab * wl.logits.element_size()
+    nvec = -(-row_bytes // 16)
+    if row_bytes % 16 or nvec > 16 * 1024:
+        return None
+    nv = 1
+    while nv * 1024 < nvec:
+        nv *= 2
+    dev = logits[0].device
+    out = torch.empty(wl.n, dtype=torch.int32, device=dev)
+    plib = probes.library()
+    args = [probes.read_rows_args(lg, wl.n, row_bytes, nv, out) for lg in logits]
+    for i in range(warmup):
+        plib.tsp_read_rows(*args[i % len(args)])
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        st = plib.tsp_read_rows(*args[(warmup + i) % len(args)])
+        if st != 0:
+            raise RuntimeError(f"tsp_read_rows failed with status {st}")
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"kernel_ms_per_launch": ms, "gbps": wl.n * row_bytes / (ms * 1e-3) / 1e9,
+            "shape": f"{wl.n} workgroups x 1024 threads x {nv} 16-byte loads"}
 
 
 def verify_inputs(wl, sampler, logits, params, gather, req, dev):
@@ -153,7 +223,8 @@ def main():
                     help="time ts_sample (default), ts_log_probs with full [n, V] rows, "
                          "ts_raw_log_probs_at at the sampled ids, or ts_verify_chain over the "
                          "decode requests of the speculative workload (spec_mix)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="CPU-seconds of oracle work for the baseline (over all its workers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -305,6 +376,11 @@ def main():
     wall = time.perf_counter() - t0
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
 
+    last_offset = args.warmup + args.steps - 1
+    ceiling = None
+    if verify is None and args.call == "sample":
+        ceiling = read_ceiling(wl, logits, args.steps, min(args.warmup, 5))
+
     rows = wl.n if verify is None else verify["bs"] * verify["n"]
     rows_per_s = rows * args.steps / wall
     gbps = (logits_bytes(wl) if verify is None else 0) * args.steps / wall / 1e9
@@ -335,13 +411,26 @@ def main():
                      "traffic": measured_traffic(args.workload) if args.call == "sample" else None,
                      "kernel_ms_per_launch": kernel_ms},
     }
+    if ceiling is not None:
+        out["roofline"]["read_ceiling"] = ceiling
+        out["roofline"]["pct_of_read_ceiling"] = 100.0 * ceiling["kernel_ms_per_launch"] / kernel_ms
     if verify is not None:
         out["config"]["verify"] = {"requests": verify["bs"], "rows_per_request": verify["n"],
                                    "mean_accepted_drafts": float(alen.float().mean().item())}
         out["roofline"]["bound"] = "launch"
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = (verify_cpu_baseline(verify, args.cpu_budget) if verify is not None
-                               else cpu_baseline(wl, args.cpu_budget, args.call))
+        if verify is not None:
+            out["cpu_baseline"] = verify_cpu_baseline(verify, args.cpu_budget)
+        else:
+            if args.call == "sample":
+                gpu_out = (ids.cpu().numpy(), lps.cpu().numpy())
+            elif args.call == "raw_log_probs":
+                gpu_out = raw.cpu().numpy()
+            else:
+                gpu_out = full.cpu().numpy()
+            out["cpu_baseline"], out["parity"] = cpu_baseline_and_parity(
+                wl, args.cpu_budget, args.call, gpu_out, last_offset,
+                token_ids=tok.cpu().numpy() if args.call == "raw_log_probs" else None)
     print(json.dumps(out), flush=True)
 
 

@@ -21,10 +21,10 @@ def lib():
     return tsa.library()
 
 
-def _declared():
-    text = open(HEADER).read()
+def _declared(header=HEADER, prefix="ts_"):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ts_[a-z_0-9]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(" + prefix + r"[a-z_0-9]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -32,6 +32,23 @@ def test_exports_every_declared_symbol(lib):
     assert "ts_sample" in names and "ts_log_probs" in names
     for name in names:
         assert hasattr(lib, name), name
+
+
+def test_probe_library_exports_and_checks_arguments(lib):
+    from token_sampling_scaled_amd import probes
+    plib = probes.library()
+    names = _declared(os.path.join(ROOT, "include", "tsprobe.h"), "tsp_")
+    assert names == ["tsp_empty", "tsp_gumbel_table", "tsp_read_rows"]
+    for name in names:
+        assert hasattr(plib, name), name
+    # argument errors come back before any HIP call
+    assert plib.tsp_empty(0, None) == 1
+    assert plib.tsp_gumbel_table(None, None, None) == 1
+    assert plib.tsp_read_rows(None, 4, 256, 256, 1, FAKE, None) == 1
+    assert plib.tsp_read_rows(FAKE, 4, 250, 256, 1, FAKE, None) == 1       # not 16-byte rows
+    assert plib.tsp_read_rows(FAKE, 4, 16 * 1024 * 2, 16 * 1024 * 2, 1, FAKE, None) == 1
+    assert plib.tsp_read_rows(FAKE, 4, 256, 256, 3, FAKE, None) == 1
+    assert plib.tsp_read_rows(FAKE, 0, 256, 256, 1, FAKE, None) == 1
 
 
 def test_status_strings_and_routes(lib):

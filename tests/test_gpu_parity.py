@@ -55,33 +55,49 @@ def test_log_probs_parity_small(name, rows, vocab):
     assert np.allclose(at[fin], lps[fin], atol=1e-5, rtol=0)
 
 
-@pytest.mark.parametrize("name", ["tiny_joint", "none_32k", "topk_128k", "joint_128k",
-                                  "topp_152k", "spec_mix"])
-def test_sample_parity_full_size_sampled_rows(name):
+@pytest.fixture(scope="module")
+def oracle_pool():
+    from oracle.parallel import Pool
+    with Pool() as pool:
+        pool.warm()
+        yield pool
+
+
+FULL = ["tiny_joint", "none_32k", "topk_128k", "joint_128k", "topp_152k", "spec_mix"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_sample_parity_full_size_every_row(name, oracle_pool):
+    """Every row of every workload at its full size, in the launch configuration
+    the benchmark times: ids and fused log-probs against the oracle (run over a
+    process pool)."""
     wl = synth.make(name)
     print(f"[case] full {name} rows={wl.n} vocab={wl.vocab}", flush=True)
     ids, lps = parity.gpu_sample(wl)
-    rows = sorted(set(np.linspace(0, wl.n - 1, 10).astype(int).tolist()))
-    rep = parity.compare_samples(ids, lps, parity.oracle_sample(wl, rows=rows), rows=rows)
-    rep.check()
+    rep = parity.compare_samples(ids, lps, parity.oracle_sample_pool(oracle_pool, wl))
+    rep.check(f"sample {name} full")
     assert np.all((ids >= 0) & (ids < wl.vocab))
 
 
-@pytest.mark.parametrize("name", ["topk_128k", "joint_128k"])
-def test_log_probs_full_size_sampled_rows(name):
-    """Full [n, V] log-probs at the benchmark size (register-resident bf16 path),
-    checked on ten rows spread over the batch; then the same at the sampled ids."""
+@pytest.mark.parametrize("name", FULL)
+def test_log_probs_full_size_every_row(name, oracle_pool):
+    """Full [n, V] log-probs of every row at the full sizes (the register-resident
+    bf16 kernel on the top-k and joint routes, the general kernel elsewhere),
+    then the same at the sampled ids."""
     wl = synth.make(name)
     print(f"[case] log_probs full {name} rows={wl.n} vocab={wl.vocab}", flush=True)
     gpu = parity.gpu_log_probs(wl)
-    rows = sorted(set(np.linspace(0, wl.n - 1, 10).astype(int).tolist()))
-    ref = parity.oracle_log_probs(wl, rows=rows)
-    res = parity.oracle_sample(wl, rows=rows)
-    parity.compare_log_probs(gpu, ref, res, rows=rows).check()
+    ref = parity.oracle_log_probs_pool(oracle_pool, wl)
+    res = parity.oracle_sample_pool(oracle_pool, wl)
+    parity.compare_log_probs(gpu, ref, res).check(f"log_probs {name} full")
+    del ref
+    # at the sampled ids: the log-prob kernel's value equals its own full row;
+    # the sampling kernel's fused value (another kernel on some routes, with
+    # its own fp32 sums) agrees within the parity tolerance
     ids, lps = parity.gpu_sample(wl)
     at = parity.gpu_log_probs(wl, token_ids=torch.from_numpy(ids.astype(np.int32)))
-    assert np.allclose(at, lps, atol=1e-5, rtol=0)
     assert np.allclose(at, gpu[np.arange(wl.n), ids], atol=1e-5, rtol=0)
+    assert np.allclose(at, lps, atol=parity.LP_ATOL, rtol=0)
 
 
 @pytest.mark.parametrize("name,rows,vocab", SMALL)
@@ -303,7 +319,7 @@ def test_sample_speculative_matches_explicit_map():
                  token_to_request_index=dev["req"])
     assert torch.equal(a, b)
     m, n = tsa.build_spec_map(64, 32, 3, device="cuda")
-    assert n == 288 and torch.equal(m.cpu(), wl.token_to_request_index)
+    assert n == 288 and np.array_equal(m.cpu().numpy(), oracle.build_spec_map(64, 32, 3))
 
 
 def test_argument_errors_on_gpu_handle():
@@ -317,6 +333,56 @@ def test_argument_errors_on_gpu_handle():
         s.sample(x.half(), 4, prm)
     out = s.sample(x, 0, prm)
     assert out.numel() == 0
+    # caller-supplied outputs are checked before any kernel is launched
+    bad_outputs = [dict(output=torch.empty(4, dtype=torch.int32)),               # host memory
+                   dict(output=torch.empty(3, dtype=torch.int32, device="cuda")),  # too short
+                   dict(output=torch.empty(4, dtype=torch.int64, device="cuda")),  # wrong dtype
+                   dict(output=torch.empty(8, dtype=torch.int32, device="cuda")[::2]),
+                   dict(logprob_output=torch.empty(4, dtype=torch.bfloat16, device="cuda")),
+                   dict(logprob_output=torch.empty(2, dtype=torch.float32, device="cuda")),
+                   dict(logprob_output=torch.empty(4, dtype=torch.float32))]
+    for kw in bad_outputs:
+        with pytest.raises(ValueError):
+            s.sample(x, 4, prm, **kw)
+    with pytest.raises(ValueError):
+        s.sample(x.cpu(), 4, prm)                                                # host logits
+    with pytest.raises(ValueError):
+        s.log_probs(x, prm, output=torch.empty(4, 100))                          # host output
+    with pytest.raises(ValueError):
+        s.log_probs(x, prm, output=torch.empty(4, 99, device="cuda"))
+    ids = torch.zeros(4, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        s.log_probs(x, prm, token_ids=ids, output=torch.empty(4))
+    with pytest.raises(ValueError):
+        s.raw_log_probs_at(x, ids, output=torch.empty(4, device="cuda", dtype=torch.float16))
+    with pytest.raises(ValueError):
+        s.raw_log_probs_at(x, ids, output=torch.empty(4))
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("route", ["joint", "topk", "topp", "none"])
+def test_parameters_at_the_fp32_thresholds(dtype, route):
+    """Temperatures at fp32(1e-5) and the next fp32 below it, top-p at
+    fp32(1) - fp32(1e-6) and the next fp32 below it: the kernels and the oracle
+    take the same side of both thresholds (rows with a tied maximum, so a
+    greedy row and a sampled one differ)."""
+    t_thr = float(np.float32(1e-5))
+    t_below = float(np.nextafter(np.float32(t_thr), np.float32(0)))
+    p_thr = float(np.float32(1.0) - np.float32(1e-6))
+    p_below = float(np.nextafter(np.float32(p_thr), np.float32(0)))
+    rng = np.random.default_rng(5)
+    rows = rng.normal(0, 1e-4, size=(8, 2048)).astype(np.float32)
+    rows[:, [3, 700, 1500]] = 1e-3                     # a tied maximum
+    t = [t_thr, t_below, t_thr, t_below, 1.0, 1.0, 0.5, 2.0]
+    p = [p_thr, p_thr, p_below, p_below, p_thr, p_below, p_below, p_thr]
+    k = 0 if route in ("topp", "none") else 1500
+    wl = _custom(rows, dtype=dtype, k=k, p=1.0, t=1.0,
+                 no_top_k=route in ("topp", "none"), no_top_p=route in ("topk", "none"))
+    wl.temperature = torch.tensor(t, dtype=torch.float32)
+    wl.top_p = torch.tensor(p, dtype=torch.float32)
+    print(f"[case] thresholds {route} {dtype}", flush=True)
+    _run_custom(wl)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])

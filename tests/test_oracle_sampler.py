@@ -448,3 +448,28 @@ def test_verify_chain_accepts_everything_when_drafts_are_the_target_samples():
     assert np.all(acc == n - 1)
     assert np.array_equal(pred, tgt)
     assert np.array_equal(idx.reshape(-1), np.arange(bs * n))
+
+
+def test_process_pool_gives_the_single_process_results():
+    """oracle.parallel splits rows over worker processes; every row's result is
+    the one oracle.sample / oracle.log_probs computes in one process (gather,
+    request map and step offset included)."""
+    import synth
+    from oracle.parallel import Pool
+    wl = synth.make("spec_mix", rows=30, vocab=777)
+    x, prm = wl.logits_f64(), wl.params_numpy()
+    kw = dict(gather_indices=wl.gather_indices.numpy(),
+              token_to_request_index=wl.token_to_request_index.numpy())
+    one = oracle.sample(x, wl.n, prm, step_offset=3, **kw)
+    lp1 = oracle.log_probs(x, wl.n, prm, **kw)
+    with Pool(workers=3) as pool:
+        many = pool.run("sample", x, wl.n, prm, step_offset=3, light=True, **kw)
+        lpm = pool.run("log_probs", x, wl.n, prm, **kw)
+        sub = pool.run("sample", x, wl.n, prm, step_offset=3, rows=[29, 4, 4], **kw)
+    assert [(a.token, a.logprob, a.flagged) for a in one] == \
+        [(b.token, b.logprob, b.flagged) for b in many]
+    assert np.array_equal(lp1, lpm)
+    assert [a.token for a in sub] == [one[29].token, one[4].token, one[4].token]
+    # the synthetic speculative workload uses the oracle's layout
+    wl = synth.make("spec_mix")
+    assert np.array_equal(wl.token_to_request_index.numpy(), oracle.build_spec_map(64, 32, 3))

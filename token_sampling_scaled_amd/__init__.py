@@ -140,7 +140,23 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _logits_args(logits: torch.Tensor, vocab: int):
+def _check_out(t: torch.Tensor, dtype, numel: int, device, name: str,
+               shape: Optional[tuple] = None) -> None:
+    """A caller-supplied output buffer: right dtype and device, contiguous, large enough
+    (the kernels write through its raw pointer)."""
+    ok = (t.dtype == dtype and t.device == device and t.is_contiguous()
+          and (t.numel() >= numel if shape is None else tuple(t.shape) == shape))
+    if not ok:
+        want = f"shape {shape}" if shape is not None else f">= {numel} entries"
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor with {want} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def _logits_args(logits: torch.Tensor, vocab: int, device=None):
+    if device is not None and logits.device != device:
+        raise ValueError(f"logits must be on the sampler's device {device}, got {logits.device}")
+    if logits.device.type != "cuda":
+        raise ValueError(f"logits must be a GPU tensor, got {logits.device}")
     if logits.dim() != 2:
         raise ValueError("logits must be 2-D [rows, vocab]")
     if logits.dtype == torch.float32:
@@ -161,8 +177,10 @@ class Sampler:
 
     def __init__(self, vocab_size: int, max_rows: int, device=None):
         lib = library()
-        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
-            else torch.device(device)
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        if dev.type != "cuda":
+            raise ValueError(f"a Sampler lives on a GPU, got {dev}")
+        self.device = dev if dev.index is not None else torch.device("cuda", torch.cuda.current_device())
         self.vocab = int(vocab_size)
         self.max_rows = int(max_rows)
         h = ctypes.c_void_p()
@@ -188,17 +206,19 @@ class Sampler:
                step_offset: int = 0, output: Optional[torch.Tensor] = None,
                logprob_output: Optional[torch.Tensor] = None, return_logprobs: bool = False):
         """Sample n ids from rows of ``logits`` (``logits[gather_indices[:n]]`` when given)."""
-        dt, rows, stride = _logits_args(logits, self.vocab)
+        dt, rows, stride = _logits_args(logits, self.vocab, self.device)
         dev = logits.device
         gather = _index_i32(gather_indices, "gather_indices", n, dev)
         req = _index_i32(token_to_request_index, "token_to_request_index", n, dev)
         if output is None:
             output = torch.empty(n, dtype=torch.int32, device=dev)
-        elif output.dtype != torch.int32 or output.numel() < n or not output.is_contiguous():
-            raise ValueError("output must be a contiguous int32 tensor with >= n entries")
+        else:
+            _check_out(output, torch.int32, n, dev, "output")
         lp = logprob_output
         if lp is None and return_logprobs:
             lp = torch.empty(n, dtype=torch.float32, device=dev)
+        elif lp is not None:
+            _check_out(lp, torch.float32, n, dev, "logprob_output")
         p = params._struct(dev)
         _check(library().ts_sample(self._h, _ptr(logits), dt, rows, stride, int(n), _ptr(gather),
                                    _ptr(req), ctypes.byref(p), int(step_offset) & (2**64 - 1),
@@ -227,7 +247,7 @@ class Sampler:
                   token_ids: Optional[torch.Tensor] = None,
                   output: Optional[torch.Tensor] = None) -> torch.Tensor:
         """Log-probs of the processed distribution: [n, V], or [n] at ``token_ids``."""
-        dt, rows, stride = _logits_args(logits, self.vocab)
+        dt, rows, stride = _logits_args(logits, self.vocab, self.device)
         dev = logits.device
         n = rows if n is None else int(n)
         gather = _index_i32(gather_indices, "gather_indices", n, dev)
@@ -236,8 +256,8 @@ class Sampler:
         shape = (n,) if ids is not None else (n, self.vocab)
         if output is None:
             output = torch.empty(shape, dtype=torch.float32, device=dev)
-        elif output.dtype != torch.float32 or tuple(output.shape) != shape or not output.is_contiguous():
-            raise ValueError(f"output must be a contiguous float32 tensor of shape {shape}")
+        else:
+            _check_out(output, torch.float32, 0, dev, "output", shape=shape)
         p = params._struct(dev)
         _check(library().ts_log_probs(self._h, _ptr(logits), dt, rows, stride, n, _ptr(gather),
                                       _ptr(req), ctypes.byref(p), int(bool(no_top_k)),
@@ -250,15 +270,17 @@ class Sampler:
                          n: Optional[int] = None, gather_indices: Optional[torch.Tensor] = None,
                          output: Optional[torch.Tensor] = None) -> torch.Tensor:
         """[n] log-softmax of the raw rows (no temperature, no filter) at token_ids."""
-        dt, rows, stride = _logits_args(logits, self.vocab)
+        dt, rows, stride = _logits_args(logits, self.vocab, self.device)
         dev = logits.device
         n = rows if n is None else int(n)
         gather = _index_i32(gather_indices, "gather_indices", n, dev)
         ids = _index_i32(token_ids, "token_ids", n, dev)
+        if ids is None:
+            raise ValueError("token_ids is required")
         if output is None:
             output = torch.empty(n, dtype=torch.float32, device=dev)
-        elif output.dtype != torch.float32 or output.numel() < n or not output.is_contiguous():
-            raise ValueError("output must be a contiguous float32 tensor with >= n entries")
+        else:
+            _check_out(output, torch.float32, n, dev, "output")
         _check(library().ts_raw_log_probs_at(self._h, _ptr(logits), dt, rows, stride, n,
                                              _ptr(gather), _ptr(ids), _ptr(output), _stream(dev)),
                "ts_raw_log_probs_at")

@@ -1,10 +1,11 @@
-"""Build libtssample.so (gfx950) in-tree with hipcc.
+"""Build libtssample.so and libtsprobe.so (gfx950) in-tree with hipcc.
 
     python -m token_sampling_scaled_amd.build          # compile every source
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
-generation switched off, and linked with the C-ABI host code into one shared
-library next to this file.
+generation switched off.  csrc/ (kernels and the C-ABI host code) links into
+libtssample.so, the sampler; csrc_probe/ links into libtsprobe.so, the measurement
+probes that the benchmark and the GPU tests use beside it.
 """
 from __future__ import annotations
 
@@ -18,7 +19,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
+PROBE = os.path.join(PKG, "csrc_probe")
 LIB = os.path.join(PKG, "libtssample.so")
+PROBE_LIB = os.path.join(PKG, "libtsprobe.so")
 
 ARCH = "gfx950"
 HIP_FLAGS = [
@@ -35,17 +38,24 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libtssample.so")
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+def sources(folder: str = CSRC):
+    return sorted(os.path.join(folder, f) for f in os.listdir(folder) if f.endswith((".hip", ".cpp")))
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile both libraries (every call compiles every source); returns the sampler's path."""
+    _build_lib(sources(CSRC), LIB, verbose, jobs)
+    _build_lib(sources(PROBE), PROBE_LIB, verbose, jobs)
+    return LIB
+
+
+def _build_lib(srcs, lib_path: str, verbose: bool, jobs: int) -> None:
     cc = hipcc()
     objdir = tempfile.mkdtemp(prefix="tssample_build_")
     try:
         procs = []
         objs = []
-        for src in sources():
+        for src in srcs:
             obj = os.path.join(objdir, os.path.basename(src) + ".o")
             objs.append(obj)
             cmd = [cc, *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", src, "-o", obj]
@@ -58,15 +68,14 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
                 _wait(procs.pop(0))
         for p in procs:
             _wait(p)
-        tmp = LIB + ".tmp"
+        tmp = lib_path + ".tmp"
         link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
         if verbose:
             print(" ".join(link), flush=True)
         subprocess.run(link, check=True)
-        os.replace(tmp, LIB)
+        os.replace(tmp, lib_path)
     finally:
         shutil.rmtree(objdir, ignore_errors=True)
-    return LIB
 
 
 def _wait(item):

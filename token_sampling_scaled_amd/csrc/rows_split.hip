@@ -132,8 +132,7 @@ __global__ __launch_bounds__(kSplitBlock) void rows_split_none_kernel(RowArgs a,
       for (int e = 0; e < 4; ++e) {
         const float s = sv[i][e];
         sum += __builtin_amdgcn_exp2f(s - mloc);       // 0 for -inf
-        const float u = ((float)(w.v[e] >> 9) + 0.5f) * 0x1p-23f;
-        const float z = s - __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
+        const float z = s + gumbel2_from_word(w.v[e]);
         if (z > bz) {                                  // j rises: first of equals stays
           bz = z;
           bj = g * 4 + e;

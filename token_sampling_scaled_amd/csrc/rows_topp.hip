@@ -501,8 +501,7 @@ __global__ __launch_bounds__(kSplitBlock) void rows_topp_draw_kernel(RowArgs a, 
       for (int e = 0; e < 4; ++e) {
         if (!((gm >> e) & 1u)) continue;
         const float sv = ms[t][e];
-        const float u = ((float)(w.v[e] >> 9) + 0.5f) * 0x1p-23f;
-        const float zz = sv - __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
+        const float zz = sv + gumbel2_from_word(w.v[e]);
         const int32_t jj = (int32_t)(g * 4 + e);
         if (better(zz, jj, bz, bj)) {
           bz = zz;
