@@ -215,6 +215,32 @@ ts_status ts_verify_chain(int32_t bs, int32_t n_per_req, const int32_t* candidat
                           const int32_t* target_sampled, int32_t* predicts,
                           int32_t* accept_index, int32_t* accept_length, void* stream);
 
+/* Largest n that ts_sample_noalloc accepts. */
+#define TS_NOALLOC_MAX_ROWS 1024
+
+/* ts_sample without a handle and without any device allocation, for callers
+ * that cannot call hipMalloc: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments and results as
+ * ts_sample (the sampler's vocabulary is passed as `vocab`), on the current
+ * HIP device.  The scratch memory the kernels need (split-row tickets and
+ * partial results, the top-p route's per-row state; about 2.1 MB) is a
+ * fixed-size device array inside the library: each GPU the library runs on
+ * holds its own copy until the process ends.  The first call on a device
+ * looks up that copy's address and clears its tickets with a small kernel on
+ * `stream`; later calls find them at zero again, because every call leaves
+ * them so.  Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (two streams, or two host threads) race and may return wrong
+ * results; serialise them.  Inputs and outputs are the caller's, as for
+ * ts_sample; nothing is allocated or freed here.
+ * Errors: TS_E_ARG, TS_E_DTYPE, TS_E_SIZE (n > TS_NOALLOC_MAX_ROWS, and the
+ * checks of ts_sample), TS_E_HIP. */
+ts_status ts_sample_noalloc(int64_t vocab, const void* logits, ts_dtype dtype,
+                            int64_t rows_in_buffer, int64_t row_stride, int32_t n,
+                            const int32_t* gather_indices, const int32_t* token_to_request_index,
+                            const ts_params* params, uint64_t step_offset,
+                            int32_t no_top_k, int32_t no_top_p,
+                            int32_t* out_ids, float* out_logprob, void* stream);
+
 /* The route the flags select (pure host function, no GPU). */
 ts_route ts_select_route(int32_t no_top_k, int32_t no_top_p);
 
