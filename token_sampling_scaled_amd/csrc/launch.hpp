@@ -22,18 +22,36 @@ struct alignas(16) SplitPartial {
   uint32_t pad[3];
 };
 
-// Per-row state of the top-p route between its two kernels.
+// Per-row state of the top-p route between its kernels.  Masses are 64-bit
+// fixed-point integers: an entry with scaled logit s2 = x log2(e) / T weighs
+// floor(exp2(s2 - m0) * 2^shift) + 1.
 struct alignas(16) TopPRow {
-  uint32_t mode;   // 0: draw from the entries with order key >= key_c; 1: done
-  uint32_t key_c;  // order key of the cutoff tie group
-  float m2;        // row maximum of x log2(e) / T
-  float zp;        // mass of P: sum over P of exp2(s - m2)
-  int64_t src;     // source row in the logits buffer
-  uint64_t seed;   // the request's seed
-  float scale2;    // log2(e) / T
-  uint32_t pad;
-  uint64_t off;    // the request's Philox offset in this call
+  uint32_t mode;     // kTopPCut, kTopPAll (P = every entry above -inf) or kTopPDone
+  int32_t bstar;     // bucket holding the cutoff tie group (kTopPCut)
+  float top2;        // upper edge of bucket 0, in base-2 units of s2
+  float inv_w;       // buckets per base-2 unit
+  float m0;          // mass reference
+  float scale2;      // log2(e) / T
+  int32_t shift;     // fixed-point scale 2^shift
+  uint32_t nlist;    // entries of bucket bstar appended by the draw kernel
+  int64_t src;       // source row in the logits buffer
+  uint64_t seed;     // the request's seed
+  uint64_t off;      // the request's Philox offset in this call
+  uint64_t above;    // mass of the buckets above bstar (kTopPAll: the mass of P)
+  double target;     // p times the row's mass
 };
+constexpr uint32_t kTopPCut = 0;
+constexpr uint32_t kTopPDone = 1;
+constexpr uint32_t kTopPAll = 2;
+
+// One entry of a row's cutoff bucket, as the draw kernel saw it.
+struct alignas(16) TopPCand {
+  uint32_t key;      // order key
+  int32_t j;         // vocabulary index
+  float z2;          // perturbed score s2 + g2 (base-2 units)
+  float s2;          // scaled logit
+};
+constexpr int kTopPListCap = 256;   // cutoff-bucket entries kept per row
 
 // Everything a row kernel needs; all pointers are device pointers.
 struct RowArgs {
@@ -57,6 +75,7 @@ struct RowArgs {
   uint32_t* split_counter;     // workspace: [max_rows] zeros between calls
   void* split_partials;        // workspace: [max_rows * kMaxSplit] SplitPartial
   TopPRow* topp_rows;          // workspace: [max_rows]
+  TopPCand* topp_list;         // workspace: [max_rows * kTopPListCap]
   int32_t heavy_first;         // fast kernel: workgroups take the rows without a register-
                                // resident top-k body first (more rows than CUs, n <= 1024)
 };
@@ -78,7 +97,8 @@ hipError_t launch_rows_split_none(const RowArgs& a, DType dtype, hipStream_t str
 // needs split_none_supported(a).
 hipError_t launch_rows_raw_log_prob_at(const RowArgs& a, DType dtype, hipStream_t stream);
 
-// Top-p route: a cutoff kernel (one workgroup per row) and a split draw kernel.
+// Top-p route: a histogram kernel (one workgroup per row), a split draw kernel
+// and a finishing kernel (one workgroup per row).
 bool topp_supported(const RowArgs& a);
 hipError_t launch_rows_topp(const RowArgs& a, DType dtype, hipStream_t stream);
 

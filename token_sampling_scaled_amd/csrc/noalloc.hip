@@ -19,11 +19,13 @@ constexpr int32_t kRows = TS_NOALLOC_MAX_ROWS;
 constexpr size_t kCounterBytes = ((size_t)kRows * sizeof(uint32_t) + 255) & ~(size_t)255;
 constexpr size_t kPartialBytes = (size_t)kRows * tss::kMaxSplit * sizeof(tss::SplitPartial);
 constexpr size_t kTopPBytes = ((size_t)kRows * sizeof(tss::TopPRow) + 255) & ~(size_t)255;
-constexpr size_t kScratchBytes = kCounterBytes + kPartialBytes + kTopPBytes;
+constexpr size_t kListBytes = (size_t)kRows * tss::kTopPListCap * sizeof(tss::TopPCand);
+constexpr size_t kScratchBytes = kCounterBytes + kPartialBytes + kTopPBytes + kListBytes;
 static_assert(kPartialBytes % 256 == 0, "partials keep the 256-byte alignment");
 
 // Tickets (zero between calls: the workgroup that merges a row puts its
-// counter back), then the partial results, then the per-row top-p state.
+// counter back), then the partial results, then the per-row top-p state and
+// the top-p cutoff-bucket lists.
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 __global__ void zero_words(uint32_t* p, int32_t n) {
@@ -131,6 +133,7 @@ extern "C" ts_status ts_sample_noalloc(int64_t vocab, const void* logits, ts_dty
   a.split_counter = reinterpret_cast<uint32_t*>(d.ptr);
   a.split_partials = d.ptr + kCounterBytes;
   a.topp_rows = reinterpret_cast<tss::TopPRow*>(d.ptr + kCounterBytes + kPartialBytes);
+  a.topp_list = reinterpret_cast<tss::TopPCand*>(d.ptr + kCounterBytes + kPartialBytes + kTopPBytes);
   a.heavy_first = (n > d.num_cu && n <= 1024) ? 1 : 0;
   const tss::Route route = (tss::Route)ts_select_route(no_top_k, no_top_p);
   const hipError_t err =

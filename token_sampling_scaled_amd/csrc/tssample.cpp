@@ -19,6 +19,7 @@ struct ts_sampler {
   uint32_t* split_counter;
   void* split_partials;
   tss::TopPRow* topp_rows;
+  tss::TopPCand* topp_list;
   int32_t num_cu;        // compute units of the device (0 for a validation-only handle)
 };
 
@@ -95,6 +96,7 @@ tss::RowArgs make_args(const ts_sampler* s, const void* logits, int64_t row_stri
   a.split_counter = s->split_counter;
   a.split_partials = s->split_partials;
   a.topp_rows = s->topp_rows;
+  a.topp_list = s->topp_list;
   // one fast-kernel workgroup fills a CU: with more rows than CUs the rows
   // that start late should be the quick ones
   a.heavy_first = (s->num_cu > 0 && n > s->num_cu && n <= 1024) ? 1 : 0;
@@ -144,14 +146,16 @@ ts_status ts_create(int64_t vocab, int32_t max_rows, int32_t device, ts_sampler*
   s->split_counter = nullptr;
   s->split_partials = nullptr;
   s->topp_rows = nullptr;
+  s->topp_list = nullptr;
   s->num_cu = 0;
   if (device >= 0) {
     // counters, padded to 256 bytes, then the partial results, then the
-    // per-row top-p state
+    // per-row top-p state and the top-p cutoff-bucket lists
     const size_t counter_bytes = ((size_t)max_rows * sizeof(uint32_t) + 255) & ~(size_t)255;
     const size_t partial_bytes = (size_t)max_rows * tss::kMaxSplit * sizeof(tss::SplitPartial);
-    const size_t topp_bytes = (size_t)max_rows * sizeof(tss::TopPRow);
-    const size_t bytes = counter_bytes + partial_bytes + topp_bytes;
+    const size_t topp_bytes = ((size_t)max_rows * sizeof(tss::TopPRow) + 255) & ~(size_t)255;
+    const size_t list_bytes = (size_t)max_rows * tss::kTopPListCap * sizeof(tss::TopPCand);
+    const size_t bytes = counter_bytes + partial_bytes + topp_bytes + list_bytes;
     DeviceGuard guard(device);
     if (!guard.ok) {
       delete s;
@@ -179,6 +183,8 @@ ts_status ts_create(int64_t vocab, int32_t max_rows, int32_t device, ts_sampler*
     s->split_counter = static_cast<uint32_t*>(ws);
     s->split_partials = static_cast<char*>(ws) + counter_bytes;
     s->topp_rows = reinterpret_cast<tss::TopPRow*>(static_cast<char*>(ws) + counter_bytes + partial_bytes);
+    s->topp_list = reinterpret_cast<tss::TopPCand*>(static_cast<char*>(ws) + counter_bytes +
+                                                    partial_bytes + topp_bytes);
   }
   *out = s;
   return TS_OK;
