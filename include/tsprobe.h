@@ -32,9 +32,33 @@ extern "C" {
 int tsp_read_rows(const void* data, int64_t rows, int64_t row_bytes, int64_t row_stride_bytes,
                   int32_t loads_per_thread, uint32_t* out, void* stream);
 
+/* Streaming read of rows of any length: `parts` workgroups of `threads`
+ * (256, 512 or 1024) threads per row, each reading its share of the row's
+ * 16-byte vectors with a ring of 16 loads in flight per thread, non-temporal
+ * when `nontemporal` is nonzero.  out[row] (device uint32 [rows], zeroed by
+ * the caller) receives the xor of the row's words, so no load can be
+ * dropped.  The time of one call is the read ceiling of that launch shape
+ * (for the top-p route's one workgroup of 1024 threads per row, among
+ * others).  Errors: 1 (sizes not multiples of 16, bad shape, NULL), 4. */
+int tsp_read_rows_ring(const void* data, int64_t rows, int64_t row_bytes, int64_t row_stride_bytes,
+                       int32_t threads, int32_t parts, int32_t nontemporal, uint32_t* out,
+                       void* stream);
+
 /* An empty kernel of `blocks` workgroups of 1024 threads: the launch and
  * drain cost any one-launch call pays.  Errors: 1 (blocks < 1), 4. */
 int tsp_empty(int32_t blocks, void* stream);
+
+/* Noise throughput: `blocks` workgroups of 256 threads, each thread drawing
+ * `per_thread` Philox4x32-10 blocks (counter (i, thread, 0x5EED, 0), a fixed
+ * key) with the sampling kernels' own generator; with with_gumbel != 0 every
+ * word also goes through the base-2 Gumbel transform and the thread keeps the
+ * largest, as the draw kernels do.  blocks * 256 * per_thread / (time of one
+ * call) is the device's rate of noise blocks: the arithmetic bound of a
+ * kernel that draws noise for most of a row.  out: device uint32 [blocks *
+ * 256], written (what each thread kept).  Errors: 1 (blocks < 1,
+ * per_thread < 1, too many threads, NULL), 4. */
+int tsp_noise_rate(int32_t blocks, int32_t per_thread, int32_t with_gumbel, uint32_t* out,
+                   void* stream);
 
 /* The device's integer -> Gumbel noise transforms, evaluated on every one of
  * the 2^23 uniforms u_i = (i + 1/2) 2^-23 they can see (word w = i << 9):

@@ -38,12 +38,18 @@ def test_probe_library_exports_and_checks_arguments(lib):
     from token_sampling_scaled_amd import probes
     plib = probes.library()
     names = _declared(os.path.join(ROOT, "include", "tsprobe.h"), "tsp_")
-    assert names == ["tsp_empty", "tsp_gumbel_table", "tsp_read_rows"]
+    assert names == ["tsp_empty", "tsp_gumbel_table", "tsp_noise_rate", "tsp_read_rows",
+                     "tsp_read_rows_ring"]
     for name in names:
         assert hasattr(plib, name), name
     # argument errors come back before any HIP call
     assert plib.tsp_empty(0, None) == 1
     assert plib.tsp_gumbel_table(None, None, None) == 1
+    assert plib.tsp_noise_rate(0, 1, 0, FAKE, None) == 1
+    assert plib.tsp_noise_rate(4, 0, 1, FAKE, None) == 1
+    assert plib.tsp_noise_rate(4, 1, 1, None, None) == 1
+    assert plib.tsp_read_rows_ring(FAKE, 4, 256, 256, 128, 1, 0, FAKE, None) == 1   # bad block
+    assert plib.tsp_read_rows_ring(FAKE, 4, 256, 256, 256, 65, 0, FAKE, None) == 1  # parts > 64
     assert plib.tsp_read_rows(None, 4, 256, 256, 1, FAKE, None) == 1
     assert plib.tsp_read_rows(FAKE, 4, 250, 256, 1, FAKE, None) == 1       # not 16-byte rows
     assert plib.tsp_read_rows(FAKE, 4, 16 * 1024 * 2, 16 * 1024 * 2, 1, FAKE, None) == 1

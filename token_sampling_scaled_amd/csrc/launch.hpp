@@ -22,34 +22,36 @@ struct alignas(16) SplitPartial {
   uint32_t pad[3];
 };
 
-// Per-row state of the top-p route between its kernels.  Masses are 64-bit
-// fixed-point integers: an entry with scaled logit s2 = x log2(e) / T weighs
-// floor(exp2(s2 - m0) * 2^shift) + 1.
+// Per-row state of the top-p route between its kernels.  Masses are relative
+// to the reference m0 in base-2 units of the scaled logit s2 = x log2(e) / T:
+// an entry weighs exp2(s2 - m0).
 struct alignas(16) TopPRow {
   uint32_t mode;     // kTopPCut, kTopPAll (P = every entry above -inf) or kTopPDone
-  int32_t bstar;     // bucket holding the cutoff tie group (kTopPCut)
-  float top2;        // upper edge of bucket 0, in base-2 units of s2
-  float inv_w;       // buckets per base-2 unit
+  int32_t bstar;     // histogram bucket holding the cutoff tie group (kTopPCut)
+  float x_hi;        // entries with x >= x_hi lie above that bucket: members of P
+  float x_lo;        // entries with x_lo <= x < x_hi lie in it
   float m0;          // mass reference
   float scale2;      // log2(e) / T
-  int32_t shift;     // fixed-point scale 2^shift
-  uint32_t nlist;    // entries of bucket bstar appended by the draw kernel
+  float inv_w;       // buckets per base-2 unit
+  float c;           // an entry's position in the histogram is fma(s2, -inv_w, c)
+  float w;           // base-2 units per bucket, 1 / inv_w
+  uint32_t nlist;    // entries of the cutoff bucket appended by the draw kernel
   int64_t src;       // source row in the logits buffer
   uint64_t seed;     // the request's seed
   uint64_t off;      // the request's Philox offset in this call
-  uint64_t above;    // mass of the buckets above bstar (kTopPAll: the mass of P)
+  double above;      // mass of the buckets above bstar (kTopPAll: of the whole row)
   double target;     // p times the row's mass
+  double bscale;     // mass of one fixed-point unit of bucket bstar
+  unsigned long long best;   // draw: max of (order of z2) << 32 | ~index over P's members
 };
 constexpr uint32_t kTopPCut = 0;
 constexpr uint32_t kTopPDone = 1;
 constexpr uint32_t kTopPAll = 2;
 
-// One entry of a row's cutoff bucket, as the draw kernel saw it.
-struct alignas(16) TopPCand {
+// One entry of a row's cutoff bucket.
+struct alignas(8) TopPCand {
   uint32_t key;      // order key
   int32_t j;         // vocabulary index
-  float z2;          // perturbed score s2 + g2 (base-2 units)
-  float s2;          // scaled logit
 };
 constexpr int kTopPListCap = 256;   // cutoff-bucket entries kept per row
 
@@ -76,6 +78,7 @@ struct RowArgs {
   void* split_partials;        // workspace: [max_rows * kMaxSplit] SplitPartial
   TopPRow* topp_rows;          // workspace: [max_rows]
   TopPCand* topp_list;         // workspace: [max_rows * kTopPListCap]
+  int32_t num_cu;              // compute units of the device (sizes persistent grids)
   int32_t heavy_first;         // fast kernel: workgroups take the rows without a register-
                                // resident top-k body first (more rows than CUs, n <= 1024)
 };

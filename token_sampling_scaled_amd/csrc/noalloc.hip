@@ -134,6 +134,7 @@ extern "C" ts_status ts_sample_noalloc(int64_t vocab, const void* logits, ts_dty
   a.split_partials = d.ptr + kCounterBytes;
   a.topp_rows = reinterpret_cast<tss::TopPRow*>(d.ptr + kCounterBytes + kPartialBytes);
   a.topp_list = reinterpret_cast<tss::TopPCand*>(d.ptr + kCounterBytes + kPartialBytes + kTopPBytes);
+  a.num_cu = d.num_cu;
   a.heavy_first = (n > d.num_cu && n <= 1024) ? 1 : 0;
   const tss::Route route = (tss::Route)ts_select_route(no_top_k, no_top_p);
   const hipError_t err =

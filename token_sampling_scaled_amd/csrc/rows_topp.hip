@@ -1,35 +1,41 @@
 // Top-p route (every row of the call filtered by top-p only, or unfiltered):
-// three kernels; the row is read once from HBM and once more by the draw
-// (mostly from the Infinity Cache, which still holds it).
+// three kernels; the row is read once by each of the first two.
 //
-// 1. rows_topp_hist_kernel, one workgroup of 1024 threads per row:
-//    - mass reference m0 = the largest scaled logit s2 = x log2(e) / T among
-//      the first eight 4-entry groups of every thread (read before anything
-//      else);
-//    - Z = the row's mass: every entry above -inf weighs
-//      floor(exp2(s2 - m0) 2^shift) + 1 (64-bit fixed point, so every sum is
-//      independent of the order of the additions);
-//    - with top-p on, a histogram of those masses over kBuckets equal buckets
-//      of s2 in [top2 - span, top2], counted from the top: top2 = m0 + 8,
-//      span = 9 + max(0, log2(V / (1 - p))).  The entries below that range weigh less
-//      than (1 - p) Z all together (Z is at least the mass of the row's
-//      maximum, which lies within 8 of m0), so the top-p cutoff lies inside
-//      it.  The first nonempty bucket from the top whose cumulative mass
-//      reaches p Z holds the cutoff tie group: bucket b*.  A row whose maximum
-//      exceeds top2 repeats the pass with m0 = its maximum.
-// 2. rows_topp_draw_kernel, (row, tile) workgroups of 256 threads: the
-//    entries in buckets above b* are members of P; each 4-entry group holding
-//    a member, or an entry of b*, draws one Philox block.  Entries of b* are
-//    appended (order key, index, perturbed score) to the row's list.  Each tile
-//    leaves its best member as a partial result.
-// 3. rows_topp_finish_kernel, one workgroup per row: the exact cutoff inside
-//    b* from the list -- the largest key v whose entries at or above v, with
-//    the mass above b*, reach p Z (so whole tie groups stay together) -- then
-//    the best of the tiles and of the list's members, the id and its log-prob.
-//    A list that overflowed its capacity is rebuilt from the row by radix
-//    passes over the order keys of b*.
-// Greedy rows and rows with no entry above -inf are finished by the first
-// kernel.
+// 1. rows_topp_hist_kernel, one workgroup of 1024 threads per row.  With
+//    s2 = x log2(e) / T, every entry above -inf weighs exp2(s2 - m0), where the
+//    reference m0 is the largest s2 of the first 4-entry group of every thread
+//    (loaded alone, before the rest of the row, so that the wait for it is
+//    short).
+//    - A histogram over kBuckets equal buckets of s2 in [top2 - span, top2],
+//      counted from the top: top2 = m0 + kHeadroom and span = kHeadroom + 1 +
+//      max(0, log2(V / (1 - p))).  The entries below that range weigh less
+//      than (1 - p) Z all together (Z, the row's mass, is at least that of the
+//      row maximum, which lies within kHeadroom of m0), so the top-p cutoff
+//      lies inside it.  Every entry adds a fixed-point mass relative to an
+//      edge, 2^20 exp2(-(position - edge) w) rounded, with a 64-bit
+//      integer LDS atomic, so the sums do not depend on the order of the
+//      atomics: in-range entries to their bucket (edge: its upper end), the
+//      entries below the range to a spare slot of their lane (edge: the
+//      range's lower end).  A unit of a bucket weighs 2^-20 exp2(edge - m0).
+//    - The first nonempty bucket from the top whose cumulative mass reaches
+//      p Z holds the cutoff tie group: bucket b*.  Its entries are exactly
+//      those with x_lo <= x < x_hi, and those above it have x >= x_hi: both
+//      bounds are the smallest order keys past a boundary of the same
+//      (monotone) bucket function, found around a computed guess.
+//    A row whose maximum lies above top2 repeats the pass with m0 = its
+//    maximum.  Greedy rows and rows with no entry above -inf finish here.
+// 2. rows_topp_draw_kernel, one 256-thread workgroup per (row, tile) item,
+//    many more than the device holds at once: entries with x >= x_hi are
+//    members of P; each wave queues its 4-entry groups holding a member and
+//    draws one Philox block per queued group, 64 at a time.  Entries of b*
+//    are appended (order key, index) to the row's list.  Each wave's best
+//    member goes into the row's best with one 64-bit atomic maximum.
+// 3. rows_topp_finish_kernel, one workgroup per row: the exact cutoff tie
+//    group inside b* from the list -- the largest key v whose entries at or
+//    above v, with the mass above b*, reach p Z, so whole tie groups stay
+//    together -- the noise of the list's members of P, the best of them and
+//    of the draw, the id and its log-prob.  A list that overflowed its
+//    capacity is rebuilt from the row by radix passes over the order keys.
 #include "split_common.hpp"
 
 namespace tss {
@@ -42,48 +48,74 @@ constexpr int kHistBlock = 1024;
 constexpr int kHistWaves = kHistBlock / kWave;
 constexpr int kBuckets = 16384;
 constexpr int kBucketsPerThread = kBuckets / kHistBlock;
-constexpr float kHeadroom = 8.0f;     // base-2 units of s2 above m0 covered by the histogram
-constexpr int kFirstBatch = 8;        // groups per thread read before m0 is fixed
-constexpr int kDrawPT = 8;            // 4-entry groups per thread in a draw tile
-constexpr int kDrawTile = kDrawPT * kSplitBlock;
-constexpr int kCand = 16384;          // cutoff-bucket keys held in LDS (overflow path)
+constexpr float kHeadroom = 12.0f;    // base-2 units of s2 above m0 covered by the histogram
+constexpr int kRing = 16;             // groups per thread in flight in the histogram pass
+constexpr float kUnitLog2 = 20.0f;    // a mass relative to its bucket edge is held in units of 2^-20
+constexpr float kMostNegative = -3.40282347e38f;
+constexpr int kDrawBlock = 256;
+constexpr int kDrawWaves = kDrawBlock / kWave;
+constexpr int kDrawPT = 8;           // 4-entry groups per thread in a draw tile
+constexpr int kDrawTile = kDrawPT * kDrawBlock;
+constexpr int kQueue = 2 * kWave;     // queued member groups per wave
+constexpr int kFinBlock = kTopPListCap;   // one list entry per thread
+constexpr int kFinWaves = kFinBlock / kWave;
 constexpr int kRadixBins = 2048;
 
 template <typename T>
 struct KeyRaw;
 template <>
 struct KeyRaw<float> {
+  static constexpr uint32_t kLo = 0x00800000u;   // key of the most negative finite value
+  static constexpr uint32_t kHi = 0xFF800000u;   // key of +inf
   __device__ __forceinline__ static float value_of_key(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+  }
+  __device__ __forceinline__ static uint32_t key_near(float x) {   // the key of x itself
+    const uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   }
 };
 template <>
 struct KeyRaw<uint16_t> {
+  static constexpr uint32_t kLo = 0x0080u;
+  static constexpr uint32_t kHi = 0xFF80u;
   __device__ __forceinline__ static float value_of_key(uint32_t k) {
     const uint32_t raw = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
     return __uint_as_float(raw << 16);
   }
+  __device__ __forceinline__ static uint32_t key_near(float x) {   // x truncated to bf16
+    const uint32_t u = __float_as_uint(x) >> 16;
+    return (u & 0x8000u) ? (~u & 0xFFFFu) : (u | 0x8000u);
+  }
 };
 
-// Scaled logit s2 = x log2(e) / T, -inf for NaN.  Rounded products and
-// differences only (no contraction), so every kernel that recomputes a bucket
-// or a mass from the same entry gets the same bits.
+// Scaled logit s2 = x log2(e) / T; NaN reads as -inf (the maximum of NaN and
+// -inf is -inf).  A rounded product, so every kernel gets the same bits.
 __device__ __forceinline__ float scaled2(float x, float scale2) {
-  return x == x ? __fmul_rn(x, scale2) : -__builtin_inff();
+  return fmaxf(__fmul_rn(x, scale2), -__builtin_inff());
 }
 
-// Bucket of a scaled logit: 0 .. kBuckets - 1 inside the histogram's range,
-// kBuckets below it (or -inf), -1 above its top.
-__device__ __forceinline__ int bucket_of(float s2, float top2, float inv_w) {
-  if (s2 > top2) return -1;
-  const float f = __fmul_rn(__fsub_rn(top2, s2), inv_w);
-  return f < (float)kBuckets ? (int)f : kBuckets;
+// Position of a scaled logit in the histogram, (top2 - s2) inv_w, as one
+// fused multiply-add from c = top2 inv_w: bucket floor(pos) when
+// 0 <= pos < kBuckets, above the range when pos < 0, below it otherwise.
+__device__ __forceinline__ float hist_pos(float s2, float inv_w, float c) {
+  return __builtin_fmaf(s2, -inv_w, c);
 }
 
-// Fixed-point mass of an entry at most 2^8 above the reference (plus one, so
-// that every counted entry shows in a sum).
-__device__ __forceinline__ unsigned long long fixed_mass(float s2, float m0, float fx_scale) {
-  return (unsigned long long)(__builtin_amdgcn_exp2f(__fsub_rn(s2, m0)) * fx_scale) + 1ull;
+__device__ __forceinline__ int bucket_of_pos(float pos) {
+  return pos < 0.0f ? -1 : (pos < (float)kBuckets ? (int)pos : kBuckets);
+}
+
+// exp2 argument of an entry's fixed-point mass relative to its bucket's upper
+// edge: 2^20 exp2(-(pos - floor(pos)) w) lies in [2^20 2^-w, 2^20].
+__device__ __forceinline__ float unit_arg(float pos, float w) {
+  return __builtin_fmaf(-__builtin_amdgcn_fractf(pos), w, kUnitLog2);
+}
+
+__device__ __forceinline__ uint32_t unit_round(float ex) { return (uint32_t)(ex + 0.5f); }
+
+__device__ __forceinline__ uint32_t unit_mass(float pos, float w) {
+  return unit_round(__builtin_amdgcn_exp2f(unit_arg(pos, w)));
 }
 
 // 4-entry group g of the row (entries past the row read as -inf).
@@ -130,6 +162,12 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
   return v;
 }
 
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
 __device__ __forceinline__ float wave_max_f(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
@@ -139,18 +177,25 @@ __device__ __forceinline__ float wave_max_f(float v) {
 // ---------------------------------------------------------------------------
 // 1. histogram
 
+// Bucket b lives in slot b + b/16 (one unused slot after every 16): the walk
+// over the histogram after the pass, where thread t takes buckets 16t ..
+// 16t + 15 in order, then reads slots 17t + j, which lie in distinct LDS banks
+// across a wave; slots 16t + j would all share one bank pair.
+constexpr int kHistSlots = kBuckets + kBuckets / 16;
+constexpr int kHistAll = kHistSlots + kWave + kWave / 16;   // then the lanes' spare slots
+__device__ __forceinline__ uint32_t hist_slot(uint32_t b) { return b + (b >> 4); }
+
 struct HistShared {
-  unsigned long long hist[kBuckets];
-  unsigned long long wsum[kHistWaves];
-  unsigned long long wscan[kHistWaves];
+  unsigned long long h64[kHistAll];   // the buckets, then the lanes' spare slots
+  unsigned long long zb_units;        // the spare slots' sum
+  double wscan[kHistWaves];
   float wmax[kHistWaves];
-  uint32_t wovf[kHistWaves];
   uint32_t wkey[kHistWaves];
   int32_t wj[kHistWaves];
   int32_t hit;
   int32_t first;
   int32_t last;
-  unsigned long long hit_above;
+  double hit_above, hit_scale;
 };
 
 template <typename T, bool VEC>
@@ -167,13 +212,22 @@ __global__ __launch_bounds__(kHistBlock) void rows_topp_hist_kernel(RowArgs a) {
   const T* row = reinterpret_cast<const T*>(a.logits) + src * a.row_stride;
   const int64_t v = a.vocab;
   const int32_t groups = (int32_t)((v + 3) >> 2);
+
+  // the thread's first group goes out before the request's parameters are
+  // read; it alone fixes the mass reference, so that the wait for it is short
+  // (the ring of later loads is issued only after that)
+  uint32_t ring[kRing][4];
+  load_group<T, VEC>(row, v, groups, tid, ring[0]);
+
   const float temp = a.temperature[q];
   const float p = a.top_p ? a.top_p[q] : 1.0f;
   const bool greedy = !(temp >= 1e-5f);
+  const uint64_t seed = a.seed[q];
+  const uint64_t off = noise_offset(a, q);
   TopPRow* st = a.topp_rows + r;
 
   auto first_max = [&](bool nan_lp) {
-    // first index of the largest order key (NaN as -inf, -0 as +0); greedy
+    // first index of the largest order key (NaN as -inf, -0 as +0): greedy
     // rows, and rows whose maximum is +inf
     uint32_t bkey = 0;
     int32_t bj = 0x7FFFFFFF;
@@ -188,9 +242,9 @@ __global__ __launch_bounds__(kHistBlock) void rows_topp_hist_kernel(RowArgs a) {
       }
     });
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const uint32_t ok = (uint32_t)__shfl_xor((int)bkey, off, kWave);
-      const int32_t oj = __shfl_xor(bj, off, kWave);
+    for (int off2 = 32; off2 > 0; off2 >>= 1) {
+      const uint32_t ok = (uint32_t)__shfl_xor((int)bkey, off2, kWave);
+      const int32_t oj = __shfl_xor(bj, off2, kWave);
       if (ok > bkey || (ok == bkey && oj < bj)) {
         bkey = ok;
         bj = oj;
@@ -202,10 +256,10 @@ __global__ __launch_bounds__(kHistBlock) void rows_topp_hist_kernel(RowArgs a) {
     }
     __syncthreads();
     if (tid == 0) {
-      for (int w = 1; w < kHistWaves; ++w) {
-        if (sh.wkey[w] > bkey || (sh.wkey[w] == bkey && sh.wj[w] < bj)) {
-          bkey = sh.wkey[w];
-          bj = sh.wj[w];
+      for (int w2 = 1; w2 < kHistWaves; ++w2) {
+        if (sh.wkey[w2] > bkey || (sh.wkey[w2] == bkey && sh.wj[w2] < bj)) {
+          bkey = sh.wkey[w2];
+          bj = sh.wj[w2];
         }
       }
       const bool none = bj == 0x7FFFFFFF;
@@ -221,94 +275,73 @@ __global__ __launch_bounds__(kHistBlock) void rows_topp_hist_kernel(RowArgs a) {
 
   const float scale2 = 1.4426950408889634f / temp;
   const bool p_on = p < 1.0f - 1e-6f;
-  const int shift = 53 - a.index_bits < 40 ? 53 - a.index_bits : 40;
-  const float fx_scale = __builtin_ldexpf(1.0f, shift);
-  // histogram range below top2, in base-2 units: always at least the headroom
-  // and one more, so the row maximum lies inside it
+  // histogram range below top2, in base-2 units: always the headroom and one
+  // more, so the row maximum lies inside it
   const float span = kHeadroom + 1.0f +
                      fmaxf(__builtin_amdgcn_logf((float)v / fmaxf(1.0f - p, 1e-30f)), 0.0f);
   const float inv_w = (float)kBuckets / span;
+  const float w = 1.0f / inv_w;
 
-  // ---- mass reference: the largest s2 among the first groups of every thread
-  uint32_t first[kFirstBatch][4];
+  // ---- mass reference: the largest s2 of the first group of every thread
+  for (int s = tid; s < kHistAll; s += kHistBlock) sh.h64[s] = 0ull;
   float tmax = -__builtin_inff();
+  if (tid < groups) {
 #pragma unroll
-  for (int u = 0; u < kFirstBatch; ++u) {
-    const int32_t g = tid + u * kHistBlock;
-    load_group<T, VEC>(row, v, groups, g, first[u]);
-  }
-  if (p_on) {
-    for (int b = tid; b < kBuckets; b += kHistBlock) sh.hist[b] = 0ull;
-  }
-#pragma unroll
-  for (int u = 0; u < kFirstBatch; ++u) {
-    if (tid + u * kHistBlock >= groups) continue;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, scaled2(E::value(first[u][e]), scale2));
+    for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, scaled2(E::value(ring[0][e]), scale2));
   }
   tmax = wave_max_f(tmax);
   if (lane == 0) sh.wmax[wid] = tmax;
   __syncthreads();
   float m0 = sh.wmax[0];
-  for (int w = 1; w < kHistWaves; ++w) m0 = fmaxf(m0, sh.wmax[w]);
+  for (int w2 = 1; w2 < kHistWaves; ++w2) m0 = fmaxf(m0, sh.wmax[w2]);
+#pragma unroll
+  for (int u = 1; u < kRing; ++u) load_group<T, VEC>(row, v, groups, tid + u * kHistBlock, ring[u]);
 
-  // ---- the pass: Z, the histogram, the row maximum, and whether any entry
-  // lies above top2
-  unsigned long long zt = 0;
-  bool ovf = false;
-  auto add_entries = [&](const uint32_t (&raw)[4], float m0v, float top2v) {
+  // ---- the pass: every entry adds a fixed-point mass relative to an edge,
+  // 2^20 exp2(-(pos - edge) w): in-range entries to their bucket (edge =
+  // floor(pos)), the entries below the range to their lane's spare slot (edge
+  // = kBuckets, the range's lower end; lanes hit distinct banks there).  An
+  // entry just above top2 may land in bucket 0 and the ones further above in
+  // a spare slot: the row is redone then anyway.
+  float top2 = m0 + kHeadroom;
+  float c = top2 * inv_w;
+  const uint32_t spare = (uint32_t)(kBuckets + lane);
+  auto add_group = [&](const uint32_t (&raw)[4]) {
+    float s2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s2[e] = scaled2(E::value(raw[e]), scale2);
+    tmax = fmaxf(tmax, fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3])));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float s2 = scaled2(E::value(raw[e]), scale2);
-      tmax = fmaxf(tmax, s2);
-      if (!(s2 > -__builtin_inff())) continue;
-      if (s2 > top2v) {
-        ovf = true;
-        continue;
-      }
-      const unsigned long long fx = fixed_mass(s2, m0v, fx_scale);
-      zt += fx;
-      if (p_on) {
-        const int b = bucket_of(s2, top2v, inv_w);
-        if (b < kBuckets) atomicAdd(&sh.hist[b], fx);
-      }
+      const float pos = hist_pos(s2[e], inv_w, c);
+      const int bi = (int)pos;
+      const bool in = (uint32_t)bi < (uint32_t)kBuckets;
+      const float rel = in ? __builtin_amdgcn_fractf(pos) : pos - (float)kBuckets;
+      const uint32_t um = unit_round(__builtin_amdgcn_exp2f(__builtin_fmaf(-rel, w, kUnitLog2)));
+      atomicAdd(&sh.h64[hist_slot(in ? (uint32_t)bi : spare)], (unsigned long long)um);
     }
   };
-  float top2 = m0 + kHeadroom;
-  {
-#pragma unroll
-    for (int u = 0; u < kFirstBatch; ++u)
-      if (tid + u * kHistBlock < groups) add_entries(first[u], m0, top2);
-    const int32_t g_rest = tid + kFirstBatch * kHistBlock;
-    constexpr int U = 8;
-    for (int32_t g0 = g_rest; g0 < groups; g0 += U * kHistBlock) {
-      uint32_t raw[U][4];
-#pragma unroll
-      for (int u = 0; u < U; ++u) load_group<T, VEC>(row, v, groups, g0 + u * kHistBlock, raw[u]);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (g0 + u * kHistBlock < groups) add_entries(raw[u], m0, top2);
-    }
-  }
-  auto reduce = [&]() {
-    const unsigned long long zw = wave_sum_u64(zt);
+  auto row_max = [&]() {
     const float mw = wave_max_f(tmax);
-    const uint32_t ow = __ballot(ovf) ? 1u : 0u;
-    __syncthreads();   // the previous readers of the wave slots are done
-    if (lane == 0) {
-      sh.wsum[wid] = zw;
-      sh.wmax[wid] = mw;
-      sh.wovf[wid] = ow;
-    }
+    __syncthreads();   // every earlier reader of the wave slots is done; the atomics are
+    if (lane == 0) sh.wmax[wid] = mw;
     __syncthreads();
+    float mr = sh.wmax[0];
+    for (int w2 = 1; w2 < kHistWaves; ++w2) mr = fmaxf(mr, sh.wmax[w2]);
+    return mr;
   };
-  reduce();
-  float mrow = -__builtin_inff();
-  bool any_ovf = false;
-  for (int w = 0; w < kHistWaves; ++w) {
-    mrow = fmaxf(mrow, sh.wmax[w]);
-    any_ovf = any_ovf || sh.wovf[w] != 0;
+  // (with VEC every load is issued, a slot past the row re-reading its last
+  // group, so the number of loads in flight is the same at every step)
+  for (int32_t g0 = tid; g0 < groups; g0 += kRing * kHistBlock) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      const int32_t g = g0 + u * kHistBlock;
+      if (g < groups) add_group(ring[u]);
+      const int32_t gn = g + kRing * kHistBlock;
+      if (VEC || gn < groups) load_group<T, VEC>(row, v, groups, gn, ring[u]);
+    }
   }
+  float mrow = row_max();
   if (mrow == -__builtin_inff()) {            // no entry above -inf
     if (tid == 0) {
       a.out_ids[r] = -1;
@@ -318,66 +351,86 @@ __global__ __launch_bounds__(kHistBlock) void rows_topp_hist_kernel(RowArgs a) {
     return;
   }
   if (mrow == __builtin_inff()) {             // +inf in the row: the first one, lp NaN
-    __syncthreads();
     first_max(true);
     return;
   }
-  if (any_ovf) {
-    // the maximum lies more than the headroom above m0: the pass again with
-    // m0 = the row maximum (re-read from the caches)
+  if (hist_pos(mrow, inv_w, c) < 0.0f) {
+    // the maximum lies more than the headroom above m0 (pos is monotone in
+    // s2, so no other entry lies above top2 unless it does): the pass again
+    // with m0 = the row maximum (re-read from the caches)
     m0 = mrow;
     top2 = m0 + kHeadroom;
-    zt = 0;
-    ovf = false;
-    if (p_on) {
-      for (int b = tid; b < kBuckets; b += kHistBlock) sh.hist[b] = 0ull;
-    }
+    c = top2 * inv_w;
+    for (int s = tid; s < kHistAll; s += kHistBlock) sh.h64[s] = 0ull;
     __syncthreads();
     for_row_groups<T, VEC, kHistBlock>(row, v, groups, [&](int32_t, const uint32_t (&raw)[4]) {
-      add_entries(raw, m0, top2);
+      add_group(raw);
     });
-    reduce();
-  }
-  unsigned long long z = 0;
-  for (int w = 0; w < kHistWaves; ++w) z += sh.wsum[w];
-
-  const uint64_t off = noise_offset(a, q);
-  if (!p_on) {                                // P = every entry above -inf
-    if (tid == 0) {
-      st->mode = kTopPAll;
-      st->m0 = m0;
-      st->scale2 = scale2;
-      st->shift = shift;
-      st->above = z;
-      st->src = src;
-      st->seed = a.seed[q];
-      st->off = off;
-    }
-    return;
+    (void)row_max();
   }
 
-  // ---- the cutoff bucket: the first nonempty bucket from the top whose
-  // cumulative mass reaches p Z (the first nonempty one when p <= 0; the last
-  // nonempty one if rounding leaves the target unreached)
-  const double target = (double)p * (double)z;
-  unsigned long long mine = 0;
+  // ---- bucket masses.  A unit of bucket b's fixed-point sum weighs
+  // 2^-20 exp2(e_b - m0), e_b = (c - b) / inv_w its upper edge.  Thread t
+  // owns buckets 16t + j, j = 0 .. 15: bucket 16t + j weighs exp2(-j / inv_w)
+  // times bucket 16t (small arguments: single precision holds them to an
+  // ulp), and bucket 16t's exponent D - 16t / inv_w, D = c / inv_w - m0, is
+  // assembled from exact single-precision pieces (fma residuals and a
+  // two-sum) and split into an integer and a fraction before the exp2.
+  auto edge_weight = [&](int b) -> double {     // 2^-20 exp2(e_b - m0)
+    const float res = __builtin_fmaf(-w, inv_w, 1.0f);   // 1 / inv_w = w (1 + res + ...)
+    const float w_lo = w * res;
+    const float cw = c * w;
+    const float cw_lo = __builtin_fmaf(c, w, -cw);
+    const float d_hi = cw - m0;                  // two-sum of cw and -m0
+    const float bb = d_hi - cw;
+    const float d_lo = ((cw - (d_hi - bb)) + (-m0 - bb)) + cw_lo + c * w_lo;
+    const float fb = (float)b;
+    const float p_hi = fb * w;
+    const float p_lo = __builtin_fmaf(fb, w, -p_hi) + fb * w_lo;
+    const float x_hi = d_hi - p_hi;              // two-sum of d_hi and -p_hi
+    const float bb2 = x_hi - d_hi;
+    const float x_lo = ((d_hi - (x_hi - bb2)) + (-p_hi - bb2)) + (d_lo - p_lo);
+    const float n = __builtin_floorf(x_hi);
+    const float f = (x_hi - n) + x_lo;
+    return __builtin_ldexp((double)__builtin_amdgcn_exp2f(f), (int)n - (int)kUnitLog2);
+  };
+  const int b0 = tid * kBucketsPerThread;
+  const double base = edge_weight(b0);          // per-unit weight of bucket b0
+  if (wid == 0) {                               // the spare slots: the entries below the range
+    const unsigned long long zu = wave_sum_u64(sh.h64[hist_slot((uint32_t)spare)]);
+    if (lane == 0) sh.zb_units = zu;
+  }
+  // exp2(-j / inv_w), j = 0 .. 15, one per lane, read back as scalars
+  const float ej_lane = __builtin_amdgcn_exp2f(-(float)(lane & (kBucketsPerThread - 1)) * w);
+  // mass of bucket b0 + j relative to `base` (the same arithmetic wherever it
+  // is needed, from the histogram in LDS)
+  auto rel_mass = [&](int j) -> float {
+    const unsigned long long h = sh.h64[hist_slot((uint32_t)(b0 + j))];
+    const float hf = __builtin_fmaf((float)(uint32_t)(h >> 32), 4294967296.0f, (float)(uint32_t)h);
+    return hf * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ej_lane), j));
+  };
+  double mine = 0.0;
   int firstne = 0x7FFFFFFF, lastne = -1;
 #pragma unroll
-  for (int i = 0; i < kBucketsPerThread; ++i) {
-    const int b = tid * kBucketsPerThread + i;
-    const unsigned long long h = sh.hist[b];
-    mine += h;
-    if (h) {
-      firstne = min(firstne, b);
-      lastne = b;
+  for (int j = 0; j < kBucketsPerThread; ++j) {
+    const float mj = rel_mass(j);
+    mine += (double)mj;
+    if (mj != 0.0f) {
+      firstne = min(firstne, b0 + j);
+      lastne = b0 + j;
     }
   }
-  unsigned long long incl = mine;
+  mine *= base;
+  // block scan of the thread masses: thread t's interval [excl, incl] ends
+  // exactly where thread t + 1's begins
+  double incl = mine;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
-    const unsigned long long t = __shfl_up(incl, o, kWave);
+    const double t = __shfl_up(incl, o, kWave);
     if (lane >= o) incl += t;
   }
+  double excl = __shfl_up(incl, 1, kWave);
+  if (lane == 0) excl = 0.0;
   if (lane == kWave - 1) sh.wscan[wid] = incl;
   if (tid == 0) {
     sh.hit = -1;
@@ -385,176 +438,328 @@ __global__ __launch_bounds__(kHistBlock) void rows_topp_hist_kernel(RowArgs a) {
     sh.last = -1;
   }
   __syncthreads();
-  if (lastne >= 0) {
-    atomicMin(&sh.first, firstne);
-    atomicMax(&sh.last, lastne);
-  }
-  unsigned long long cum = incl - mine;
-  for (int w = 0; w < wid; ++w) cum += sh.wscan[w];
-#pragma unroll
-  for (int i = 0; i < kBucketsPerThread; ++i) {
-    const int b = tid * kBucketsPerThread + i;
-    const unsigned long long h = sh.hist[b];
-    if (h && (double)cum < target && (double)(cum + h) >= target) {
-      sh.hit = b;
-      sh.hit_above = cum;
+  {
+    // buckets rise with the thread: the wave's first nonempty bucket is its
+    // first such lane's, the last one its last such lane's (one atomic each
+    // per wave; a shared address takes its atomics one at a time)
+    const unsigned long long ne = __ballot(lastne >= 0);
+    if (ne) {
+      if (lane == __builtin_ctzll(ne)) atomicMin(&sh.first, firstne);
+      if (lane == 63 - __builtin_clzll(ne)) atomicMax(&sh.last, lastne);
     }
-    cum += h;
   }
-  __syncthreads();
-  if (tid == 0) {
-    int bstar = sh.hit;
-    unsigned long long above = sh.hit_above;
-    if (bstar < 0) {
-      if (target <= 0.0) {
-        bstar = sh.first < kBuckets ? sh.first : 0;
-        above = 0;
-      } else {
-        bstar = sh.last >= 0 ? sh.last : 0;
-        unsigned long long tot = 0;
-        for (int w = 0; w < kHistWaves; ++w) tot += sh.wscan[w];
-        above = tot - sh.hist[bstar];
+  double pre = 0.0, zin = 0.0;
+  for (int w2 = 0; w2 < kHistWaves; ++w2) {
+    if (w2 == wid) pre = zin;
+    zin += sh.wscan[w2];
+  }
+  excl += pre;
+  incl += pre;
+  const double zbelow = (double)sh.zb_units * edge_weight(kBuckets);
+  if (!p_on) {                                  // P = every entry above -inf (uniform)
+    if (tid == 0) {
+      st->mode = kTopPAll;
+      st->best = 0ull;
+      st->x_hi = kMostNegative;
+      st->x_lo = kMostNegative;
+      st->m0 = m0;
+      st->scale2 = scale2;
+      st->nlist = 0;
+      st->above = zin + zbelow;
+      st->src = src;
+      st->seed = seed;
+      st->off = off;
+    }
+    return;
+  }
+  const double target = (double)p * (zin + zbelow);
+  // the bucket b0 + j of this thread at cumulative mass `cj` when the walk
+  // reaches it (the walk adds the buckets in the order of the sum above)
+  auto walk_to = [&](int jstop, double& cj) {
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < kBucketsPerThread; ++j)
+      if (j < jstop) acc += (double)rel_mass(j);
+    cj = excl + acc * base;
+  };
+  auto publish = [&](int b, double above_b) {
+    sh.hit = b;
+    sh.hit_above = above_b;
+    sh.hit_scale = base * (double)__builtin_amdgcn_exp2f(-(float)(b - b0) * w);
+  };
+  if (excl < target && target <= incl) {
+    // the first bucket of this thread whose cumulative mass reaches the
+    // target; rounding may leave it unreached, then the last nonempty one
+    double acc = 0.0;
+    int hit = -1;
+    double hit_above = 0.0;
+#pragma unroll
+    for (int j = 0; j < kBucketsPerThread; ++j) {
+      const double cj = excl + acc * base;
+      const float mj = rel_mass(j);
+      acc += (double)mj;
+      if (mj != 0.0f && hit < 0 && excl + acc * base >= target) {
+        hit = b0 + j;
+        hit_above = cj;
       }
     }
-    st->mode = kTopPCut;
-    st->bstar = bstar;
-    st->top2 = top2;
-    st->inv_w = inv_w;
-    st->m0 = m0;
-    st->scale2 = scale2;
-    st->shift = shift;
-    st->nlist = 0;
-    st->above = above;
-    st->target = target;
-    st->src = src;
-    st->seed = a.seed[q];
-    st->off = off;
+    if (hit < 0) {
+      hit = lastne;
+      walk_to(lastne - b0, hit_above);
+    }
+    publish(hit, hit_above);
+  }
+  __syncthreads();
+  if (sh.hit < 0) {                             // uniform: the target lies outside the range's mass
+    const bool low = target <= 0.0;
+    const int bsel = low ? sh.first : sh.last;
+    if (bsel >= b0 && bsel < b0 + kBucketsPerThread) {
+      double cj = 0.0;
+      if (!low) walk_to(bsel - b0, cj);
+      publish(bsel, cj);
+    }
+    __syncthreads();
+  }
+
+  // ---- the bounds of b*'s entries: lanes 0 .. 31 look for the smallest key
+  // whose bucket lies above b*, lanes 32 .. 63 for the smallest one whose
+  // bucket is b* or above.  The bucket of a key's value never rises with the
+  // key, and +inf lies above every bucket.  The boundary value of s2 is
+  // about (c - lim - 1) / inv_w; the 32 keys around that guess are checked at
+  // once, and a binary search over every key runs only if they miss it.
+  if (wid == 0) {
+    const int bstar = sh.hit < 0 ? 0 : sh.hit;
+    const int half = lane >> 5;
+    const int lim = half == 0 ? bstar - 1 : bstar;
+    auto pred = [&](uint32_t key) {
+      return bucket_of_pos(hist_pos(scaled2(KeyRaw<T>::value_of_key(key), scale2), inv_w, c)) <= lim;
+    };
+    const float xg = ((c - (float)(lim + 1)) * w) / scale2;
+    const uint32_t kg = KeyRaw<T>::key_near(xg);
+    const uint32_t k0 = kg < KeyRaw<T>::kLo + 16u ? KeyRaw<T>::kLo
+                      : (kg > KeyRaw<T>::kHi - 15u ? KeyRaw<T>::kHi - 31u : kg - 16u);
+    const uint32_t cand = k0 + (uint32_t)(lane & 31);
+    const unsigned long long bal = __ballot(pred(cand));
+    const uint32_t hb = (uint32_t)(bal >> (half * 32));
+    uint32_t key;
+    // found when the window holds the first true key: some are true, and
+    // the first is not the window's first unless that is the smallest key
+    const bool found = hb != 0u && ((hb & 1u) == 0u || k0 == KeyRaw<T>::kLo);
+    if (found) {
+      key = k0 + (uint32_t)__builtin_ctz(hb);
+    } else {
+      uint32_t lo = KeyRaw<T>::kLo, hi = KeyRaw<T>::kHi;
+      while (lo < hi) {
+        const uint32_t mid = lo + ((hi - lo) >> 1);
+        if (pred(mid)) hi = mid;
+        else lo = mid + 1;
+      }
+      key = lo;
+    }
+    const float bound = KeyRaw<T>::value_of_key(key);
+    const float xb_hi = __shfl(bound, 0, kWave);
+    const float xb_lo = __shfl(bound, 32, kWave);
+    if (lane == 0) {
+      st->mode = kTopPCut;
+      st->best = 0ull;
+      st->bstar = bstar;
+      st->x_hi = xb_hi;
+      st->x_lo = xb_lo;
+      st->m0 = m0;
+      st->scale2 = scale2;
+      st->inv_w = inv_w;
+      st->c = c;
+      st->w = w;
+      st->nlist = 0;
+      st->above = sh.hit_above;
+      st->target = target;
+      st->bscale = sh.hit_scale;
+      st->src = src;
+      st->seed = seed;
+      st->off = off;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // 2. draw
 
-// Tile `tile` of row r: members of P (buckets above b*, or every entry above
-// -inf when P is the whole row) and the entries of b*; each wave compacts its
-// groups that hold one, then draws one Philox block per compacted group.
-template <typename T, bool VEC, int PT>
-__global__ __launch_bounds__(kSplitBlock) void rows_topp_draw_kernel(RowArgs a, int32_t ntiles) {
+// One workgroup per (row, tile) item (item = tile * n + r, so that the rows'
+// tiles interleave), many more items than the device holds at once: the
+// hardware deals them out as workgroups finish, which keeps the compute units
+// evenly loaded however unevenly the members of P fall over the rows.  The
+// tile's loads go out first.  Entries with x >= x_hi are members of P: each
+// wave queues its groups holding a member in LDS and draws one Philox block
+// per queued group, 64 at a time.  Entries of the cutoff bucket (x_lo <= x <
+// x_hi) are appended to the row's list, one atomic per wave for its slots.
+// Each wave's best member goes into the row's best with one 64-bit atomic
+// maximum of (order of z2, complement of its index).
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kDrawBlock) void rows_topp_draw_kernel(RowArgs a, int32_t ntiles) {
   using E = SplitElem<T>;
   using K = typename E::Key;
-  __shared__ uint32_t cg[kSplitWaves][PT * kWave];        // group << 8 | boundary mask << 4 | member mask
-  __shared__ uint32_t craw[kSplitWaves][PT * kWave][4];   // the group's raw entries
-  __shared__ Best sbest[kSplitWaves];
+  __shared__ uint32_t qg[kDrawWaves][kQueue];        // queued groups
+  __shared__ uint32_t qraw[kDrawWaves][kQueue][4];   // their raw entries
 
   const int r = (int)(blockIdx.x % (uint32_t)a.n);
   const int tile = (int)(blockIdx.x / (uint32_t)a.n);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wid = tid / kWave;
-  TopPRow* st = a.topp_rows + r;
-  const uint32_t mode = st->mode;
-  if (mode == kTopPDone) return;                 // uniform over the workgroup
-  const bool all = mode == kTopPAll;
-  const int bstar = st->bstar;
-  const float top2 = st->top2;
-  const float inv_w = st->inv_w;
-  const float scale2 = st->scale2;
-  const T* row = reinterpret_cast<const T*>(a.logits) + st->src * a.row_stride;
-  const uint64_t seed = st->seed;
-  const uint64_t off = st->off;
-  const NoiseStream ns{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r, (uint32_t)off,
-                       (uint32_t)(off >> 32)};
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int64_t v = a.vocab;
   const int32_t groups = (int32_t)((v + 3) >> 2);
   const int32_t t0 = tile * kDrawTile;
   const int32_t t_end = t0 + kDrawTile < groups ? t0 + kDrawTile : groups;
+  const int64_t src = a.gather ? (int64_t)a.gather[r] : (int64_t)r;
+  const T* row = reinterpret_cast<const T*>(a.logits) + src * a.row_stride;
 
-  uint32_t raw[PT][4];
+  // the tile's loads go out before the row's state is read
+  uint32_t raw[kDrawPT][4];
 #pragma unroll
-  for (int i = 0; i < PT; ++i) {
-    const int32_t g = t0 + tid + i * kSplitBlock;
-    load_group<T, VEC>(row, v, t_end, g, raw[i]);
-  }
-  uint32_t fill = 0;
-#pragma unroll
-  for (int i = 0; i < PT; ++i) {
-    const int32_t g = t0 + tid + i * kSplitBlock;
-    uint32_t mm = 0, bm = 0;
-    if (g < t_end) {
+  for (int i = 0; i < kDrawPT; ++i) load_group<T, VEC>(row, v, t_end, t0 + tid + i * kDrawBlock, raw[i]);
+
+  // the row's state through the constant address space: scalar loads
+  // (nothing this kernel writes is read this way)
+  const __attribute__((address_space(4))) TopPRow* st =
+      (const __attribute__((address_space(4))) TopPRow*)(a.topp_rows + r);
+  if (st->mode == kTopPDone) return;             // uniform over the workgroup
+  const float x_hi = st->x_hi;
+  const float x_lo = st->x_lo;
+  const float scale2 = st->scale2;
+  const uint64_t seed = st->seed;
+  const uint64_t off = st->off;
+  const NoiseStream ns{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r, (uint32_t)off,
+                       (uint32_t)(off >> 32)};
+
+  float bz = -__builtin_inff();                  // this lane's best member: z2, index
+  int32_t bj = 0x7FFFFFFF;
+  uint32_t fill = 0;                             // queued groups of this wave (uniform)
+  auto drain = [&](uint32_t count) {             // draw the first count (<= 64) queued groups
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if ((uint32_t)lane < count) {
+      const uint32_t g = qg[wid][lane];
+      const Philox4 wd = ns.block(g);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float s2 = scaled2(E::value(raw[i][e]), scale2);
-        if (all) {
-          mm |= (s2 > -__builtin_inff() ? 1u : 0u) << e;
-        } else {
-          const int b = bucket_of(s2, top2, inv_w);
-          mm |= (b < bstar ? 1u : 0u) << e;
-          bm |= (b == bstar ? 1u : 0u) << e;
+        const float x = E::value(qraw[wid][lane][e]);
+        if (!(x >= x_hi)) continue;
+        // members are finite: x * scale2 needs no NaN guard
+        const float z2 = x * scale2 + gumbel2_from_word(wd.v[e]);
+        const int32_t j = (int32_t)(g * 4 + e);
+        if (z2 > bz || (z2 == bz && j < bj)) {
+          bz = z2;
+          bj = j;
         }
       }
     }
-    const bool has = (mm | bm) != 0;
-    const unsigned long long bal = __ballot(has);
-    if (has) {
-      const uint32_t pos = fill + lane_rank_u64(bal);
-      cg[wid][pos] = ((uint32_t)g << 8) | (bm << 4) | mm;
+  };
+  unsigned long long bnd_any = 0ull;             // lanes with a cutoff-bucket entry
 #pragma unroll
-      for (int e = 0; e < 4; ++e) craw[wid][pos][e] = raw[i][e];
-    }
-    fill += (uint32_t)__popcll(bal);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-  Best best{0u, 0x7FFFFFFF, 0.0f};
-  TopPCand* list = a.topp_list + (int64_t)r * kTopPListCap;
-  for (uint32_t t = lane; t < fill; t += kWave) {
-    const uint32_t c = cg[wid][t];
-    const uint32_t g = c >> 8;
-    const Philox4 w = ns.block(g);
+  for (int i = 0; i < kDrawPT; ++i) {
+    const int32_t g = t0 + tid + i * kDrawBlock;
+    // lane masks (scalar): groups holding a member, and groups holding an
+    // entry of the cutoff bucket (x >= x_lo but not x >= x_hi)
+    const unsigned long long valid = __ballot(g < t_end);
+    unsigned long long memm = 0ull, bndm = 0ull;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const bool mem = (c >> e) & 1u;
-      const bool bnd = (c >> (4 + e)) & 1u;
-      if (!(mem || bnd)) continue;
-      const uint32_t rw = craw[wid][t][e];
-      const float s2 = scaled2(E::value(rw), scale2);
-      const float z2 = s2 + gumbel2_from_word(w.v[e]);
-      const int32_t j = (int32_t)(g * 4 + e);
-      if (mem) {
-        const uint32_t o = order_of(z2);
-        if (beats(o, j, best.o, best.j)) best = Best{o, j, s2};
-      } else {
-        const uint32_t slot = atomicAdd(&st->nlist, 1u);
-        if (slot < (uint32_t)kTopPListCap) list[slot] = TopPCand{K::from_bits(rw), j, z2, s2};
+      const float x = E::value(raw[i][e]);
+      const unsigned long long hi = __ballot(x >= x_hi);
+      memm |= hi;
+      bndm |= __ballot(x >= x_lo) ^ hi;
+    }
+    memm &= valid;
+    bnd_any |= bndm & valid;
+    if ((memm >> lane) & 1ull) {
+      const uint32_t pos = fill + lane_rank_u64(memm);
+      qg[wid][pos] = (uint32_t)g;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qraw[wid][pos][e] = raw[i][e];
+    }
+    fill += (uint32_t)__popcll(memm);
+    if (fill >= (uint32_t)kWave) {               // a full round of 64 groups: draw it
+      drain(kWave);
+      fill -= kWave;
+      uint32_t mg = 0, m4[4] = {0u, 0u, 0u, 0u};
+      if ((uint32_t)lane < fill) {                // move the rest to the front
+        mg = qg[wid][kWave + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m4[e] = qraw[wid][kWave + lane][e];
+      }
+      __builtin_amdgcn_wave_barrier();
+      if ((uint32_t)lane < fill) {
+        qg[wid][lane] = mg;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qraw[wid][lane][e] = m4[e];
       }
     }
   }
-  best = wave_best(best);
-  if (lane == 0) sbest[wid] = best;
-  __syncthreads();
-  if (tid == 0) {
-    Best b = sbest[0];
+  if (fill) drain(fill);
+
+  // the cutoff bucket's entries (a few per row): one atomic per wave
+  // reserves their slots in the row's list
+  if (bnd_any) {
+    uint32_t nb = 0;
+    uint32_t bmask[kDrawPT];
 #pragma unroll
-    for (int w = 1; w < kSplitWaves; ++w)
-      if (beats(sbest[w].o, sbest[w].j, b.o, b.j)) b = sbest[w];
-    SplitPartial* pp = reinterpret_cast<SplitPartial*>(a.split_partials) + (int64_t)r * ntiles + tile;
-    pp->o = b.o;
-    pp->j = b.j;
-    pp->s = b.s;
+    for (int i = 0; i < kDrawPT; ++i) {
+      const int32_t g = t0 + tid + i * kDrawBlock;
+      uint32_t bm = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = E::value(raw[i][e]);
+        bm |= (g < t_end && x >= x_lo && !(x >= x_hi) ? 1u : 0u) << e;
+      }
+      bmask[i] = bm;
+      nb += (uint32_t)__popc(bm);
+    }
+    uint32_t incl = nb;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t t = (uint32_t)__shfl_up((int)incl, o, kWave);
+      if (lane >= o) incl += t;
+    }
+    uint32_t base = 0;
+    if (lane == kWave - 1) base = atomicAdd(&a.topp_rows[r].nlist, incl);
+    base = (uint32_t)__shfl((int)base, kWave - 1, kWave) + incl - nb;
+    TopPCand* list = a.topp_list + (int64_t)r * kTopPListCap;
+    // (static indexes only: an index into raw[] known only at run time
+    // would put the whole tile in scratch memory)
+#pragma unroll
+    for (int i = 0; i < kDrawPT; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if ((bmask[i] >> e) & 1u) {
+          if (base < (uint32_t)kTopPListCap)
+            list[base] = TopPCand{K::from_bits(raw[i][e]), (t0 + tid + i * kDrawBlock) * 4 + e};
+          ++base;
+        }
+      }
+    }
   }
+  // the wave's best: the largest (order of z2, -index)
+  unsigned long long key =
+      bj == 0x7FFFFFFF ? 0ull
+                       : ((unsigned long long)order_of(bz) << 32) | (unsigned long long)(~(uint32_t)bj);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long t = __shfl_xor(key, o, kWave);
+    key = t > key ? t : key;
+  }
+  if (lane == 0 && key != 0ull) atomicMax(&a.topp_rows[r].best, key);
 }
 
 // ---------------------------------------------------------------------------
 // 3. finish
 
 struct FinShared {
+  alignas(16) uint2 ent[kTopPListCap];   // the list: (order key, fixed-point mass)
   unsigned long long mass[kRadixBins];   // radix bins (overflow path)
-  uint32_t cand[kCand];
-  unsigned long long wtot[kHistWaves];
-  Best wbest[kHistWaves];
-  uint32_t ncand;
+  unsigned long long wtot[kFinWaves];
+  double wz[kFinWaves];
+  Best wbest[kFinWaves];
   int32_t hit;
   int32_t first;
   int32_t last;
@@ -563,16 +768,17 @@ struct FinShared {
 };
 
 // In bins [0, nb) ordered from the largest keys down, the first nonempty bin
-// whose cumulative mass, on top of `base`, reaches `target` (the first
-// nonempty bin when base already does; the last nonempty bin if none does).
-// Writes the bin, the mass above it and its own mass to LDS (valid after the
-// call in every thread).
+// whose cumulative mass, on top of `base` units and the mass `above`,
+// reaches `target` (the first nonempty bin when base already does; the last
+// nonempty bin if none does).  Bin masses are fixed-point units worth `unit`
+// each.  Writes the bin, the units above it and its own units to LDS (valid
+// after the call in every thread).
 __device__ __forceinline__ void find_crossing(FinShared& sh, int nb, unsigned long long base,
-                                              double target) {
+                                              double above, double unit, double target) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wid = tid / kWave;
-  const int per = nb / kHistBlock;
+  const int per = nb / kFinBlock;
   unsigned long long mine = 0;
   int lastne = -1, firstne = 0x7FFFFFFF;
   for (int i = 0; i < per; ++i) {
@@ -605,7 +811,7 @@ __device__ __forceinline__ void find_crossing(FinShared& sh, int nb, unsigned lo
   for (int i = 0; i < per; ++i) {
     const int b = tid * per + i;
     const unsigned long long m = sh.mass[b];
-    if (m && (double)cum < target && (double)(cum + m) >= target) {
+    if (m && above + (double)cum * unit < target && above + (double)(cum + m) * unit >= target) {
       sh.hit = b;
       sh.hit_above = cum - base;
       sh.hit_mass = m;
@@ -613,7 +819,7 @@ __device__ __forceinline__ void find_crossing(FinShared& sh, int nb, unsigned lo
     cum += m;
   }
   __syncthreads();
-  if ((double)base >= target) {
+  if (above + (double)base * unit >= target) {
     if (tid == 0) {
       const int b = sh.first < nb ? sh.first : 0;
       sh.hit = b;
@@ -625,7 +831,7 @@ __device__ __forceinline__ void find_crossing(FinShared& sh, int nb, unsigned lo
     if (tid == 0) {
       const int b = sh.last;
       unsigned long long tot = 0;
-      for (int w = 0; w < kHistWaves; ++w) tot += sh.wtot[w];
+      for (int w = 0; w < kFinWaves; ++w) tot += sh.wtot[w];
       sh.hit = b;
       sh.hit_mass = b >= 0 ? sh.mass[b] : 0ull;
       sh.hit_above = tot - sh.hit_mass;
@@ -634,24 +840,32 @@ __device__ __forceinline__ void find_crossing(FinShared& sh, int nb, unsigned lo
   }
 }
 
-// id and log-prob: lp = (s2 - log2(sum over P of exp2(s2))) ln 2, with the sum
-// held as zp = sum of fixed-point masses (scale 2^shift, reference m0).
+// id and log-prob: lp = (s2 - m0 - log2(mass of P)) ln 2.
 __device__ __forceinline__ void write_row(const RowArgs& a, int r, const Best& b, float m0,
-                                          unsigned long long zp, int shift) {
+                                          double zp) {
   if (b.j == 0x7FFFFFFF) {            // cannot happen: P holds the row maximum
     a.out_ids[r] = -1;
     if (a.out_lp) a.out_lp[r] = __builtin_nanf("");
     return;
   }
   a.out_ids[r] = b.j;
-  if (a.out_lp) {
-    const float lz = __builtin_amdgcn_logf((float)zp) - (float)shift;
-    a.out_lp[r] = (b.s - m0 - lz) * 0.69314718055994531f;
-  }
+  if (a.out_lp) a.out_lp[r] = (float)(((double)b.s - (double)m0 - log2(zp)) * 0.69314718055994531);
+}
+
+// Block-wide best (valid in thread 0).
+__device__ __forceinline__ Best block_best(Best b, FinShared& sh) {
+  b = wave_best(b);
+  const int wid = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) sh.wbest[wid] = b;
+  __syncthreads();
+  Best o = sh.wbest[0];
+  for (int w = 1; w < kFinWaves; ++w)
+    if (beats(sh.wbest[w].o, sh.wbest[w].j, o.o, o.j)) o = sh.wbest[w];
+  return o;
 }
 
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kHistBlock) void rows_topp_finish_kernel(RowArgs a, int32_t ntiles) {
+__global__ __launch_bounds__(kFinBlock) void rows_topp_finish_kernel(RowArgs a) {
   using E = SplitElem<T>;
   using K = typename E::Key;
   __shared__ FinShared sh;
@@ -659,195 +873,146 @@ __global__ __launch_bounds__(kHistBlock) void rows_topp_finish_kernel(RowArgs a,
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wid = tid / kWave;
+
+  // the row's state and its whole list capacity are read at once
   const TopPRow* st = a.topp_rows + r;
+  const TopPCand mine_c = a.topp_list[(int64_t)r * kTopPListCap + tid];
   const uint32_t mode = st->mode;
   if (mode == kTopPDone) return;
   const float m0 = st->m0;
-  const float scale2 = st->scale2;
-  const float fx_scale = __builtin_ldexpf(1.0f, st->shift);
-  const unsigned long long above = st->above;
-  const uint32_t nlist = mode == kTopPCut ? st->nlist : 0u;
-  const bool overflow = nlist > (uint32_t)kTopPListCap;
-
-  // best of the tiles (wave 0)
+  // the draw's best member (thread 0): its order word, its index, and its
+  // scaled logit read back from the row
   Best tb{0u, 0x7FFFFFFF, 0.0f};
-  if (wid == 0) {
-    const SplitPartial* parts = reinterpret_cast<const SplitPartial*>(a.split_partials) +
-                                (int64_t)r * ntiles;
-    for (int t0 = 0; t0 < ntiles; t0 += kWave) {
-      Best b{0u, 0x7FFFFFFF, 0.0f};
-      if (t0 + lane < ntiles) {
-        const SplitPartial* pp = parts + t0 + lane;
-        b = Best{pp->o, pp->j, pp->s};
-      }
-      b = wave_best(b);
-      if (beats(b.o, b.j, tb.o, tb.j)) tb = b;
-    }
+  if (tid == 0 && st->best != 0ull) {
+    const unsigned long long bk = st->best;
+    const int32_t j = (int32_t)~(uint32_t)bk;
+    const T* brow = reinterpret_cast<const T*>(a.logits) + st->src * a.row_stride;
+    tb = Best{(uint32_t)(bk >> 32), j, scaled2(E::value(E::raw_at(brow, j)), st->scale2)};
   }
   if (mode == kTopPAll) {
-    if (tid == 0) write_row(a, r, tb, m0, above, st->shift);
+    tb = block_best(tb, sh);
+    if (tid == 0) write_row(a, r, tb, m0, st->above);
     return;
   }
+  const uint32_t nlist = st->nlist;
+  const float scale2 = st->scale2;
+  const float inv_w = st->inv_w;
+  const float c = st->c;
+  const float w = st->w;
+  const double above = st->above;
   const double target = st->target;
+  const double bscale = st->bscale;
+  const NoiseStream ns{(uint32_t)st->seed, (uint32_t)(st->seed >> 32), (uint32_t)r,
+                       (uint32_t)st->off, (uint32_t)(st->off >> 32)};
 
-  if (!overflow) {
-    // ---- the list holds every entry of b*: one wave finds the cutoff key
-    // v* = the largest key with (entries >= v* exist and) above + mass(>= v*)
-    // >= target, by a bitwise descent from the leading bits all keys share
-    if (wid != 0) return;
-    constexpr int kPer = kTopPListCap / kWave;
-    const TopPCand* list = a.topp_list + (int64_t)r * kTopPListCap;
-    uint32_t key[kPer];
-    unsigned long long fx[kPer];
-    uint32_t kmax = 0, kmin = 0xFFFFFFFFu;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const uint32_t t = (uint32_t)(i * kWave + lane);
-      key[i] = 0;
-      fx[i] = 0;
-      if (t < nlist) {
-        key[i] = list[t].key;
-        fx[i] = fixed_mass(list[t].s2, m0, fx_scale);
-        kmax = max(kmax, key[i]);
-        kmin = min(kmin, key[i]);
-      }
+  if (nlist <= (uint32_t)kTopPListCap) {
+    // ---- the list holds every entry of b*: entry i is in P when the mass
+    // above b* plus that of the list's entries with a strictly larger key
+    // stays below the target (whole tie groups together); the row's top
+    // group is always kept
+    const bool in = (uint32_t)tid < nlist;
+    float s2 = 0.0f;
+    uint32_t um = 0;
+    if (in) {
+      s2 = scaled2(KeyRaw<T>::value_of_key(mine_c.key), scale2);
+      um = unit_mass(hist_pos(s2, inv_w, c), w);
     }
-    kmax = wave_max_u32(kmax);
-    kmin = wave_min_u32(kmin);
-    auto reach = [&](uint32_t trial) -> bool {
-      unsigned long long m = 0;
-      uint32_t c = 0;
+    sh.ent[tid] = make_uint2(in ? mine_c.key : 0u, um);   // slots past the list weigh 0
+    __syncthreads();
+    unsigned long long gt = 0;
+    if (in) {
+      // eight entries per step, read as 16-byte words
+      const uint4* e4 = reinterpret_cast<const uint4*>(sh.ent);
+      for (uint32_t t = 0; t < nlist; t += 8) {
+        uint4 q[4];
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        if ((uint32_t)(i * kWave + lane) < nlist && key[i] >= trial) {
-          m += fx[i];
-          ++c;
+        for (int i = 0; i < 4; ++i) q[i] = e4[(t >> 1) + i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          gt += q[i].x > mine_c.key ? (unsigned long long)q[i].y : 0ull;
+          gt += q[i].z > mine_c.key ? (unsigned long long)q[i].w : 0ull;
         }
       }
-      m = wave_sum_u64(m);
-      c = (uint32_t)__popcll(__ballot(c != 0));
-      return c != 0 && (double)(above + m) >= target;
-    };
-    uint32_t vstar = kmin;              // kmin always reaches: every entry counts
-    if (nlist > 0 && kmax != kmin) {
-      const uint32_t diff = kmax ^ kmin;
-      const int top = 31 - __builtin_clz(diff);
-      uint32_t prefix = kmax & ~((2u << top) - 1u);
-      for (int b = top; b >= 0; --b) {
-        const uint32_t trial = prefix | (1u << b);
-        if (reach(trial)) prefix = trial;
-      }
-      vstar = prefix < kmin ? kmin : prefix;
-    } else if (nlist > 0) {
-      vstar = kmax;
     }
-    unsigned long long zp = 0;
-    Best lb{0u, 0x7FFFFFFF, 0.0f};
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const uint32_t t = (uint32_t)(i * kWave + lane);
-      if (t < nlist && key[i] >= vstar) {
-        zp += fx[i];
-        const TopPCand c = list[t];
-        const uint32_t o = order_of(c.z2);
-        if (beats(o, c.j, lb.o, lb.j)) lb = Best{o, c.j, c.s2};
-      }
+    const bool keep = in && (above + (double)gt * bscale < target || (above == 0.0 && gt == 0));
+    double zw = keep ? (double)um * bscale : 0.0;
+    Best lb = tb;
+    if (keep) {
+      const float z2 = s2 + gumbel2_from_word(ns.word((uint32_t)mine_c.j));
+      const uint32_t o = order_of(z2);
+      if (beats(o, mine_c.j, lb.o, lb.j)) lb = Best{o, mine_c.j, s2};
     }
-    zp = wave_sum_u64(zp);
-    lb = wave_best(lb);
-    if (beats(lb.o, lb.j, tb.o, tb.j)) tb = lb;
-    if (lane == 0) write_row(a, r, tb, m0, above + zp, st->shift);
+    zw = wave_sum_f64(zw);
+    if (lane == 0) sh.wz[wid] = zw;
+    lb = block_best(lb, sh);
+    if (tid == 0) {
+      double zp = above;
+      for (int w2 = 0; w2 < kFinWaves; ++w2) zp += sh.wz[w2];
+      write_row(a, r, lb, m0, zp);
+    }
     return;
   }
 
-  // ---- overflow: the order keys of b*'s entries from the row (gathered in
-  // LDS when they fit), a radix select over them on the cumulative mass, then
-  // the noise of b*'s members of P from the row
-  const int bstar = st->bstar;
-  const float top2 = st->top2;
-  const float inv_w = st->inv_w;
+  // ---- overflow: radix passes over the order keys of b*'s entries read from
+  // the row, on the cumulative mass, then the noise of b*'s members of P
+  const float x_hi = st->x_hi;
+  const float x_lo = st->x_lo;
   const T* row = reinterpret_cast<const T*>(a.logits) + st->src * a.row_stride;
   const int64_t v = a.vocab;
   const int32_t groups = (int32_t)((v + 3) >> 2);
-  if (tid == 0) sh.ncand = 0;
-  __syncthreads();
-  for_row_groups<T, VEC, kHistBlock>(row, v, groups, [&](int32_t, const uint32_t (&raw)[4]) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (bucket_of(scaled2(E::value(raw[e]), scale2), top2, inv_w) == bstar) {
-        const uint32_t slot = atomicAdd(&sh.ncand, 1u);
-        if (slot < (uint32_t)kCand) sh.cand[slot] = K::from_bits(raw[e]);
-      }
-    }
-  });
-  __syncthreads();
-  const uint32_t nc = sh.ncand;
-  const bool from_lds = nc <= (uint32_t)kCand;
   uint32_t prefix = 0;
-  unsigned long long base = above, zp_fx = 0;
+  unsigned long long base = 0, zp_units = 0;
   constexpr int kShift[3] = {21, 10, 0};
   constexpr int kBits[3] = {11, 11, 10};
 #pragma unroll 1
   for (int pass = 0; pass < 3; ++pass) {
     const int shf = kShift[pass], bits = kBits[pass];
-    for (int b = tid; b < kRadixBins; b += kHistBlock) sh.mass[b] = 0;
+    for (int b = tid; b < kRadixBins; b += kFinBlock) sh.mass[b] = 0;
     __syncthreads();
-    auto add_key = [&](uint32_t key) {
-      if (pass > 0 && (key >> (shf + bits)) != prefix) return;
-      const int d = (int)((key >> shf) & ((1u << bits) - 1u));
-      const float s2 = __fmul_rn(KeyRaw<T>::value_of_key(key), scale2);
-      atomicAdd(&sh.mass[(kRadixBins - 1) - d], fixed_mass(s2, m0, fx_scale));
-    };
-    if (from_lds) {
-      for (uint32_t t = tid; t < nc; t += kHistBlock) add_key(sh.cand[t]);
-    } else {
-      for_row_groups<T, VEC, kHistBlock>(row, v, groups, [&](int32_t, const uint32_t (&raw)[4]) {
+    for_row_groups<T, VEC, kFinBlock>(row, v, groups, [&](int32_t, const uint32_t (&raw)[4]) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (bucket_of(scaled2(E::value(raw[e]), scale2), top2, inv_w) == bstar)
-            add_key(K::from_bits(raw[e]));
-      });
-    }
+      for (int e = 0; e < 4; ++e) {
+        const float x = E::value(raw[e]);
+        if (!(x >= x_lo && x < x_hi)) continue;
+        const uint32_t key = K::from_bits(raw[e]);
+        if (pass > 0 && (key >> (shf + bits)) != prefix) continue;
+        const int d = (int)((key >> shf) & ((1u << bits) - 1u));
+        atomicAdd(&sh.mass[(kRadixBins - 1) - d],
+                  (unsigned long long)unit_mass(hist_pos(scaled2(x, scale2), inv_w, c), w));
+      }
+    });
     __syncthreads();
-    find_crossing(sh, kRadixBins, base, target);
+    find_crossing(sh, kRadixBins, base, above, bscale, target);
     const int d = (kRadixBins - 1) - (sh.hit < 0 ? 0 : sh.hit);
     base += sh.hit_above;
     prefix = (prefix << bits) | (uint32_t)d;
-    zp_fx = base + sh.hit_mass;
+    zp_units = base + sh.hit_mass;
     __syncthreads();
   }
   const uint32_t vstar = prefix;
-  const NoiseStream ns{(uint32_t)st->seed, (uint32_t)(st->seed >> 32), (uint32_t)r,
-                       (uint32_t)st->off, (uint32_t)(st->off >> 32)};
-  Best b{0u, 0x7FFFFFFF, 0.0f};
-  for_row_groups<T, VEC, kHistBlock>(row, v, groups, [&](int32_t g, const uint32_t (&raw)[4]) {
+  for_row_groups<T, VEC, kFinBlock>(row, v, groups, [&](int32_t g, const uint32_t (&raw)[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float s2 = scaled2(E::value(raw[e]), scale2);
-      if (bucket_of(s2, top2, inv_w) != bstar || K::from_bits(raw[e]) < vstar) continue;
+      const float x = E::value(raw[e]);
+      if (!(x >= x_lo && x < x_hi) || K::from_bits(raw[e]) < vstar) continue;
       const int32_t j = g * 4 + e;
+      const float s2 = scaled2(x, scale2);
       const float z2 = s2 + gumbel2_from_word(ns.word((uint32_t)j));
       const uint32_t o = order_of(z2);
-      if (beats(o, j, b.o, b.j)) b = Best{o, j, s2};
+      if (beats(o, j, tb.o, tb.j)) tb = Best{o, j, s2};
     }
   });
-  b = wave_best(b);
-  if (lane == 0) sh.wbest[wid] = b;
-  __syncthreads();
-  if (tid == 0) {
-    for (int w = 0; w < kHistWaves; ++w)
-      if (beats(sh.wbest[w].o, sh.wbest[w].j, tb.o, tb.j)) tb = sh.wbest[w];
-    write_row(a, r, tb, m0, zp_fx, st->shift);
-  }
+  tb = block_best(tb, sh);
+  if (tid == 0) write_row(a, r, tb, m0, above + (double)zp_units * bscale);
+  (void)lane;
 }
 
 template <typename T, bool VEC>
 hipError_t launch_typed(const RowArgs& a, int32_t ntiles, hipStream_t stream) {
   hipLaunchKernelGGL((rows_topp_hist_kernel<T, VEC>), dim3(a.n), dim3(kHistBlock), 0, stream, a);
-  hipLaunchKernelGGL((rows_topp_draw_kernel<T, VEC, kDrawPT>), dim3((uint32_t)a.n * ntiles),
-                     dim3(kSplitBlock), 0, stream, a, ntiles);
-  hipLaunchKernelGGL((rows_topp_finish_kernel<T, VEC>), dim3(a.n), dim3(kHistBlock), 0, stream, a,
-                     ntiles);
+  hipLaunchKernelGGL((rows_topp_draw_kernel<T, VEC>), dim3((uint32_t)a.n * ntiles), dim3(kDrawBlock),
+                     0, stream, a, ntiles);
+  hipLaunchKernelGGL((rows_topp_finish_kernel<T, VEC>), dim3(a.n), dim3(kFinBlock), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -856,8 +1021,7 @@ hipError_t launch_typed(const RowArgs& a, int32_t ntiles, hipStream_t stream) {
 bool topp_supported(const RowArgs& a) {
   const int64_t groups = (a.vocab + 3) >> 2;
   const int64_t tiles = (groups + kDrawTile - 1) / kDrawTile;
-  return a.topp_rows != nullptr && a.topp_list != nullptr && a.split_partials != nullptr &&
-         tiles <= kMaxSplit && (int64_t)a.n * tiles < 0x7FFFFFFF;
+  return a.topp_rows != nullptr && a.topp_list != nullptr && (int64_t)a.n * tiles < 0x7FFFFFFF;
 }
 
 hipError_t launch_rows_topp(const RowArgs& a, DType dtype, hipStream_t stream) {

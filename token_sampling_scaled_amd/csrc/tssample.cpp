@@ -99,6 +99,7 @@ tss::RowArgs make_args(const ts_sampler* s, const void* logits, int64_t row_stri
   a.topp_list = s->topp_list;
   // one fast-kernel workgroup fills a CU: with more rows than CUs the rows
   // that start late should be the quick ones
+  a.num_cu = s->num_cu;
   a.heavy_first = (s->num_cu > 0 && n > s->num_cu && n <= 1024) ? 1 : 0;
   return a;
 }

@@ -26,9 +26,12 @@ def library() -> ctypes.CDLL:
     lib = ctypes.CDLL(PROBE_LIB_PATH)
     c_i32, c_i64, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
     lib.tsp_read_rows.argtypes = [c_vp, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp]
+    lib.tsp_read_rows_ring.argtypes = [c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp]
     lib.tsp_empty.argtypes = [c_i32, c_vp]
     lib.tsp_gumbel_table.argtypes = [c_vp, c_vp, c_vp]
-    for name in ("tsp_read_rows", "tsp_empty", "tsp_gumbel_table"):
+    lib.tsp_noise_rate.argtypes = [c_i32, c_i32, c_i32, c_vp, c_vp]
+    for name in ("tsp_read_rows", "tsp_read_rows_ring", "tsp_empty", "tsp_gumbel_table",
+                 "tsp_noise_rate"):
         getattr(lib, name).restype = c_i32
     _lib = lib
     return lib
@@ -58,8 +61,26 @@ def read_rows(data: torch.Tensor, n: int, row_bytes: int, loads_per_thread: int,
            "tsp_read_rows")
 
 
+def read_rows_ring_args(data: torch.Tensor, n: int, row_bytes: int, threads: int, parts: int,
+                       nontemporal: bool, out: torch.Tensor):
+    """Argument list of one tsp_read_rows_ring call over the first n rows of ``data``."""
+    stride = data.stride(0) * data.element_size()
+    return [ctypes.c_void_p(data.data_ptr()), int(n), int(row_bytes), int(stride), int(threads),
+            int(parts), int(bool(nontemporal)), ctypes.c_void_p(out.data_ptr()),
+            _stream(data.device)]
+
+
 def empty(blocks: int, device) -> None:
     _check(library().tsp_empty(int(blocks), _stream(device)), "tsp_empty")
+
+
+def noise_rate(blocks: int, per_thread: int, with_gumbel: bool, out: torch.Tensor) -> None:
+    """Launch the noise throughput probe on the current stream (out: int32 [blocks * 256])."""
+    if out.dtype != torch.int32 or not out.is_cuda or out.numel() < blocks * 256:
+        raise ValueError("out must be a CUDA int32 tensor of at least blocks * 256 elements")
+    _check(library().tsp_noise_rate(blocks, per_thread, 1 if with_gumbel else 0,
+                                    ctypes.c_void_p(out.data_ptr()), _stream(out.device)),
+           "tsp_noise_rate")
 
 
 def gumbel_table(device="cuda"):
