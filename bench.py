@@ -211,6 +211,27 @@ def verify_cpu_baseline(verify, budget_s: float):
                       f"one process ({dt:.2f} s)"}
 
 
+def mask_cpu_baseline(originals, mask_words, gpu_masked, budget_s: float):
+    """The oracle's vocabulary mask (python loops, one process) over rows of the
+    same buffer until about ``budget_s`` seconds (at most 2 s: it is slow per
+    entry), compared bit for bit with the GPU's masked rows."""
+    import oracle
+    x = originals.double().numpy()
+    got = gpu_masked.double().numpy()
+    t0 = time.perf_counter()
+    rows = 0
+    mismatches = 0
+    while rows < x.shape[0] and (rows == 0 or time.perf_counter() - t0 < min(budget_s, 2.0)):
+        want = oracle.apply_vocab_mask(x[rows:rows + 1], mask_words[rows:rows + 1])
+        mismatches += int(not np.array_equal(want[0], got[rows]))
+        rows += 1
+    dt = time.perf_counter() - t0
+    base = {"value": rows / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"the first {rows} rows of the buffer, python loops over entries, one "
+                      f"process ({dt:.2f} s)"}
+    return base, {"rows": rows, "mismatches": mismatches}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,10 +240,12 @@ def main():
     ap.add_argument("--workload", default="joint_128k", choices=sorted(synth.WORKLOAD_IDS))
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0: auto)")
     ap.add_argument("--call", default="sample",
-                    choices=("sample", "log_probs", "raw_log_probs", "verify_chain"),
+                    choices=("sample", "log_probs", "raw_log_probs", "verify_chain", "vocab_mask"),
                     help="time ts_sample (default), ts_log_probs with full [n, V] rows, "
                          "ts_raw_log_probs_at at the sampled ids, or ts_verify_chain over the "
-                         "decode requests of the speculative workload (spec_mix)")
+                         "decode requests of the speculative workload (spec_mix), or "
+                         "ts_apply_vocab_mask in place over the whole logits buffer with a seeded "
+                         "mask allowing each entry with probability 1/2")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="CPU-seconds of oracle work for the baseline (over all its workers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -324,6 +347,32 @@ def main():
             if st != tsa.TS_OK:
                 raise RuntimeError(f"ts_raw_log_probs_at failed with status {st}")
 
+    mask = None
+    if args.call == "vocab_mask":
+        # one mask row per buffer row, each bit set with probability 1/2; masking
+        # is idempotent, so the rotating copies can be masked again every step
+        nb = logits[0].shape[0]
+        mrng = np.random.default_rng(9)
+        mask_words = mrng.integers(0, 2**32, size=(nb, (wl.vocab + 31) // 32), dtype=np.int64)
+        mask = torch.from_numpy(mask_words.astype(np.uint32).view(np.int32)).to(dev)
+        originals = logits[0].cpu()
+
+        def step_checked(i):
+            tsa.apply_vocab_mask(logits[i % copies], mask)
+
+        m_args = [[wl.vocab, ctypes.c_void_p(lg.data_ptr()), dt_code, lg.shape[0], lg.stride(0),
+                   ctypes.c_void_p(mask.data_ptr()), mask.stride(0), None, stream_ptr]
+                  for lg in logits]
+        ts_mask = lib.ts_apply_vocab_mask
+
+        def step(i):
+            st = ts_mask(*m_args[i % copies])
+            if st != tsa.TS_OK:
+                raise RuntimeError(f"ts_apply_vocab_mask failed with status {st}")
+
+        # every 16-byte vector holds allowed and masked entries: each is read and written
+        nbytes = 2 * nb * wl.vocab * wl.logits.element_size() + mask.numel() * 4
+
     verify = None
     if args.call == "verify_chain":
         if wl.token_to_request_index is None:
@@ -418,8 +467,14 @@ def main():
         out["config"]["verify"] = {"requests": verify["bs"], "rows_per_request": verify["n"],
                                    "mean_accepted_drafts": float(alen.float().mean().item())}
         out["roofline"]["bound"] = "launch"
+    if mask is not None:
+        out["config"]["rows"] = int(logits[0].shape[0])
+        out["value"] = logits[0].shape[0] * args.steps / wall
     if not args.no_cpu_baseline:
-        if verify is not None:
+        if mask is not None:
+            out["cpu_baseline"], out["parity"] = mask_cpu_baseline(
+                originals, mask_words, logits[0].cpu(), args.cpu_budget)
+        elif verify is not None:
             out["cpu_baseline"] = verify_cpu_baseline(verify, args.cpu_budget)
         else:
             if args.call == "sample":

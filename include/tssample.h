@@ -223,7 +223,8 @@ ts_status ts_verify_chain(int32_t bs, int32_t n_per_req, const int32_t* candidat
  * loops, harnesses that forbid allocation.  Same arguments and results as
  * ts_sample (the sampler's vocabulary is passed as `vocab`), on the current
  * HIP device.  The scratch memory the kernels need (split-row tickets and
- * partial results, the top-p route's per-row state; about 2.1 MB) is a
+ * partial results, the top-p route's per-row state and cutoff lists; about
+ * 4.2 MB) is a
  * fixed-size device array inside the library: each GPU the library runs on
  * holds its own copy until the process ends.  The first call on a device
  * looks up that copy's address and clears its tickets with a small kernel on
@@ -240,6 +241,32 @@ ts_status ts_sample_noalloc(int64_t vocab, const void* logits, ts_dtype dtype,
                             const ts_params* params, uint64_t step_offset,
                             int32_t no_top_k, int32_t no_top_p,
                             int32_t* out_ids, float* out_logprob, void* stream);
+
+/* Vocabulary mask, applied to the logits in place before sampling (the
+ * TokenSpeed Triton sampling backend page applies a vocab_mask to the logits
+ * after its NaN guard and before the greedy or Gumbel step; the mask's body is
+ * not printed there).  For every row r of the buffer (0 <= r < rows) with mask
+ * row m = mask_index ? mask_index[r] : r, entry j < vocab keeps its logit when
+ * bit (j mod 32) of mask[m * mask_stride_words + j / 32] is 1 and is set to
+ * -inf when it is 0; entries past vocab (a padded row_stride) are not touched.
+ * Every route then treats a masked entry as any other -inf entry (never
+ * sampled; a row left with no finite entry yields id -1 and lp NaN).
+ *   vocab              entries per row
+ *   logits             device bf16 or fp32 [rows, row_stride], modified in place
+ *   dtype              TS_BF16 or TS_F32
+ *   rows, row_stride   rows to mask, elements between rows (>= vocab)
+ *   mask               device uint32 [mask rows, mask_stride_words]
+ *   mask_stride_words  words between mask rows (>= ceil(vocab / 32))
+ *   mask_index         device int32 [rows] or NULL (then mask row r for row r;
+ *                      with it, e.g. one mask per request for speculative rows)
+ *   stream             hipStream_t
+ * Needs no handle and allocates nothing.  Errors: TS_E_ARG (vocab < 1 or
+ * >= 2^31, rows < 0, NULL logits or mask with rows > 0), TS_E_DTYPE,
+ * TS_E_SIZE (row_stride < vocab, mask_stride_words < ceil(vocab / 32)),
+ * TS_E_HIP. */
+ts_status ts_apply_vocab_mask(int64_t vocab, void* logits, ts_dtype dtype, int64_t rows,
+                              int64_t row_stride, const uint32_t* mask, int64_t mask_stride_words,
+                              const int32_t* mask_index, void* stream);
 
 /* The route the flags select (pure host function, no GPU). */
 ts_route ts_select_route(int32_t no_top_k, int32_t no_top_p);

@@ -18,7 +18,8 @@ What it follows (page titles as printed at the top of each page):
   distribution).
 * the TokenSpeed Triton sampling backend source page
   (``runtime/sampling/backends/triton.py``): per-request seed pools, Gumbel-max
-  sampling, the "top-p disabled when p is within eps of 1" test.
+  sampling, the "top-p disabled when p is within eps of 1" test, and the
+  vocabulary mask applied before sampling (``oracle/vocab_mask.py``).
 
 Every floating-point step is fp64.  Where the pages leave a step open, the
 reading taken is stated in the docstring of the function that takes it.
@@ -50,10 +51,11 @@ from .sampler import (
     NEAR_TIE_REL,
 )
 from .verify import verify_chain
+from .vocab_mask import apply_vocab_mask
 
 __all__ = [
     "philox4x32_10", "noise_words", "uniform_from_words", "gumbel_from_uniform",
     "RowParams", "RowResult", "order_key_sort", "top_k_mask", "top_p_mask",
     "process_row", "sample_row", "sample", "raw_log_probs_at", "log_probs", "build_spec_map",
-    "GREEDY_T_MAX", "TOP_P_EPS", "NEAR_TIE_REL", "verify_chain",
+    "GREEDY_T_MAX", "TOP_P_EPS", "NEAR_TIE_REL", "verify_chain", "apply_vocab_mask",
 ]

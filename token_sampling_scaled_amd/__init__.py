@@ -68,11 +68,12 @@ def library() -> ctypes.CDLL:
     lib.ts_build_spec_map.argtypes = [c_i32, c_i32, c_i32, c_vp, c_i32, c_i32, c_vp,
                                       ctypes.POINTER(c_i32)]
     lib.ts_verify_chain.argtypes = [c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
+    lib.ts_apply_vocab_mask.argtypes = [c_i64, c_vp, c_i32, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp]
     lib.ts_select_route.argtypes = [c_i32, c_i32]
     lib.ts_status_str.argtypes = [c_i32]
     lib.ts_status_str.restype = ctypes.c_char_p
     for name in ("ts_create", "ts_destroy", "ts_sample", "ts_log_probs", "ts_raw_log_probs_at",
-                 "ts_build_spec_map", "ts_verify_chain", "ts_select_route"):
+                 "ts_build_spec_map", "ts_verify_chain", "ts_apply_vocab_mask", "ts_select_route"):
         getattr(lib, name).restype = ctypes.c_int32
     _lib = lib
     return lib
@@ -335,5 +336,27 @@ def verify_chain(candidates: torch.Tensor, target_sampled: torch.Tensor, *,
     return predicts, accept_index, accept_length
 
 
+def apply_vocab_mask(logits: torch.Tensor, mask: torch.Tensor,
+                     mask_index: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Set to -inf, in place, every entry of ``logits`` [rows, V] (bf16 or fp32, on a
+    GPU) whose bit in the row's mask is 0: bit (j % 32) of word j // 32 of mask row
+    ``mask_index[r]`` (or r), ``mask`` int32/uint32 bits as an int32 tensor
+    [mask rows, >= ceil(V / 32)] on the same device (ts_apply_vocab_mask).  Returns
+    ``logits``."""
+    dt, rows, stride = _logits_args(logits, int(logits.shape[1]) if logits.dim() == 2 else -1)
+    dev = logits.device
+    if mask.dtype != torch.int32 or mask.device != dev or mask.dim() != 2 or mask.stride(1) != 1:
+        raise ValueError(f"mask must be a 2-D int32 tensor with contiguous rows on {dev}")
+    if mask.shape[1] < (int(logits.shape[1]) + 31) // 32:
+        raise ValueError(f"mask rows need at least ceil(V / 32) = {(int(logits.shape[1]) + 31) // 32} words")
+    idx = _index_i32(mask_index, "mask_index", rows, dev)
+    if idx is None and mask.shape[0] < rows:
+        raise ValueError(f"mask has {mask.shape[0]} rows, logits have {rows}")
+    _check(library().ts_apply_vocab_mask(int(logits.shape[1]), _ptr(logits), dt, rows, stride,
+                                         _ptr(mask), int(mask.stride(0)), _ptr(idx), _stream(dev)),
+           "ts_apply_vocab_mask")
+    return logits
+
+
 __all__ = ["Sampler", "SamplingParams", "build_spec_map", "verify_chain", "select_route",
-           "library", "LIB_PATH"]
+           "apply_vocab_mask", "library", "LIB_PATH"]
