@@ -55,6 +55,22 @@ def test_log_probs_parity_small(name, rows, vocab):
     assert np.allclose(at[fin], lps[fin], atol=1e-5, rtol=0)
 
 
+def test_bf16_top_p_route_log_probs():
+    """bf16 rows on the top-p-only route: full log-probs and log-probs at the
+    sampled ids come from the register-resident body (exact key histogram)."""
+    wl = synth.make("topp_152k", rows=8, vocab=30000)
+    wl.logits = wl.logits.to(torch.bfloat16)
+    print(f"[case] log_probs bf16 top-p rows={wl.n} vocab={wl.vocab}", flush=True)
+    gpu = parity.gpu_log_probs(wl)
+    res = parity.oracle_sample(wl)
+    parity.compare_log_probs(gpu, parity.oracle_log_probs(wl), res).check("log_probs bf16 top-p")
+    ids, lps = parity.gpu_sample(wl)
+    parity.compare_samples(ids, lps, res).check("sample bf16 top-p")
+    at = parity.gpu_log_probs(wl, token_ids=torch.from_numpy(ids.astype(np.int32)))
+    fin = ids >= 0
+    assert np.allclose(at[fin], lps[fin], atol=1e-5, rtol=0)
+
+
 @pytest.fixture(scope="module")
 def oracle_pool():
     from oracle.parallel import Pool

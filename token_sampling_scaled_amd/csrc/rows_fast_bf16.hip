@@ -520,15 +520,18 @@ __device__ __forceinline__ float key_value(uint32_t key) {
   return __uint_as_float(bits << 16);
 }
 
-// A sampled row without an active top-k, whole row in registers (d).  P is
-// every finite entry, or with top-p the tie groups from the top whose mass
-// before them stays below p * Z.  Returns false when the row needs the general
+// A row without an active top-k, whole row in registers (d).  P is every
+// finite entry, or with top-p the tie groups from the top whose mass before
+// them stays below p * Z.  Then, by MODE: the perturbed argmax over P (sample),
+// every entry's log-prob of the processed distribution written from the
+// registers (full rows: one read and one write of the row), or the log-prob
+// at the request's token id.  Returns false when the row needs the general
 // body instead (NaN or +inf in the row, or a top-p cutoff below the window of
 // 32768 order keys under the row maximum); the caller then synchronises first.
 // Every pass works on the raw order keys of two entries at a time (packed
 // 16-bit maxima, minima and saturated differences); -0 and +0, whose keys
 // differ by one, are told apart only where an entry is counted or drawn.
-template <int NV>
+template <int NV, int MODE>
 __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int nfull, const v4u (&d)[NV],
                         float inv_t, bool p_on, float pq, uint64_t seed, uint64_t off,
                         RowShared& sh) {
@@ -566,8 +569,23 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
   kmx = wave_max_dpp(lane < kWv ? ns_.wkey[lane] : 0u);
   const uint32_t any_nan_lo = wave_max_dpp(lane < kWv ? ns_.wnan[lane] : 0u);
   if (kmx >= kPosInfKey || any_nan_lo != 0) return false;   // NaN or +inf: general body
-  if (kmx <= kNegInfKey) {                        // no finite entry
-    if (tid == 0) write_result(a, r, -1, __builtin_nanf(""));
+  if (kmx <= kNegInfKey) {                        // no finite entry: id -1 and lp NaN
+    if (MODE == kOutSample) {
+      if (tid == 0) write_result(a, r, -1, __builtin_nanf(""));
+    } else if (MODE == kOutLogProbAt) {
+      if (tid == 0) a.out_lp[r] = __builtin_nanf("");
+    } else {                                      // a NaN row of log-probs
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      f32x4* out_row = reinterpret_cast<f32x4*>(a.out_lp + (int64_t)r * a.vocab);
+      const float qn = __builtin_nanf("");
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int vi = i * kB + tid;
+        if (!(i < nfull || vi < nvec)) continue;
+        out_row[2 * vi] = f32x4{qn, qn, qn, qn};
+        out_row[2 * vi + 1] = f32x4{qn, qn, qn, qn};
+      }
+    }
     return true;
   }
   // base-2 units: s2 = x log2(e) / T; exp2(s2 - m2) = exp(x / T - m)
@@ -683,12 +701,52 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
     zp = ns_.zp;
   }
 
-  // ---- Philox noise for the members of P (canonical key >= vc_key: raw key
-  // >= vc_key, and -0 too when the cutoff group is +0's), perturbed argmax
-  const NoiseStream nst{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
-                        (uint32_t)off, (uint32_t)(off >> 32)};
+  // the members of P: canonical key >= vc_key, that is raw key >= raw_thr
+  // (-0 too when the cutoff group is +0's)
   const uint32_t raw_thr = vc_key == kPosZeroKey ? kNegZeroKey : vc_key;
   const uint32_t below_m = (raw_thr - 1u) * 0x10001u;
+  if (MODE != kOutSample) {
+    // lp = x / T - m - ln Z_P on P, -inf elsewhere
+    const float lzp = __logf(zp);
+    auto lp_of_key = [&](uint32_t k) -> float {
+      return k >= raw_thr ? __fmul_rn(key_value(k), inv_t) - m - lzp : -__builtin_inff();
+    };
+    if (MODE == kOutLogProbAt) {
+      if (tid == 0) {
+        const int64_t j = a.token_ids[r];
+        float out = -__builtin_inff();
+        if (j >= 0 && j < a.vocab) {
+          const int64_t src = a.gather ? (int64_t)a.gather[r] : (int64_t)r;
+          const uint16_t rb = reinterpret_cast<const uint16_t*>(a.logits)[src * a.row_stride + j];
+          out = lp_of_key(keys2((uint32_t)rb) & 0xFFFFu);
+        }
+        a.out_lp[r] = out;
+      }
+      return true;
+    }
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    f32x4* out_row = reinterpret_cast<f32x4*>(a.out_lp + (int64_t)r * a.vocab);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int vi = i * kB + tid;
+      if (!(i < nfull || vi < nvec)) continue;
+      float o[8];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t k2 = keys2(word_of(d[i], w));
+        o[2 * w] = lp_of_key(k2 & 0xFFFFu);
+        o[2 * w + 1] = lp_of_key(k2 >> 16);
+      }
+      // plain stores (the L2 merges the two halves of every line)
+      out_row[2 * vi] = f32x4{o[0], o[1], o[2], o[3]};
+      out_row[2 * vi + 1] = f32x4{o[4], o[5], o[6], o[7]};
+    }
+    return true;
+  }
+
+  // ---- Philox noise for the members of P, perturbed argmax
+  const NoiseStream nst{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
+                        (uint32_t)off, (uint32_t)(off >> 32)};
   Pick best{-__builtin_inff(), 0x7FFFFFFF, 0.0f};
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -822,10 +880,10 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   const bool k_on = kHasK && kq >= 1 && (int64_t)kq < a.vocab;
   const bool p_on = kHasP && pq < 1.0f - 1e-6f;
 
-  // Rows without top-k draw noise for every entry (VALU-bound: nothing to gain
-  // from register residency), k above kMaxK, and greedy rows asked for
-  // log-probs: general body.
-  const bool nok = MODE == kOutSample && !greedy && !k_on;   // register-resident, below
+  // Rows without top-k: register-resident, below (noise for P, or the
+  // log-probs written from the registers).  k above kMaxK, and greedy rows
+  // asked for log-probs: general body.
+  const bool nok = !greedy && !k_on;
   if ((!greedy && !nok && (!k_on || kq > kMaxK)) || (greedy && MODE != kOutSample)) {
     general::general_row<uint16_t, ROUTE, MODE>(a, r, sh.g);
     return;
@@ -841,7 +899,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
       greedy_row<NV>(a, r, nvec, d, fs);
       return;
     }
-    if (!nok_row<NV>(a, r, nvec, nfull, d, 1.0f / temp, p_on, pq, seed, noise_offset(a, q), sh)) {
+    if (!nok_row<NV, MODE>(a, r, nvec, nfull, d, 1.0f / temp, p_on, pq, seed, noise_offset(a, q), sh)) {
       __syncthreads();
       general::general_row<uint16_t, ROUTE, MODE>(a, r, sh.g);
     }
@@ -1179,18 +1237,38 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
 template <int NV>
 hipError_t launch_nv(const RowArgs& a, Route route, OutMode mode, hipStream_t stream) {
   const dim3 grid(a.n), block(kB);
-  if (mode == kOutLogProbFull) {        // top-k and joint routes only
-    if (route == kRouteTopK)
-      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteTopK, kOutLogProbFull>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteJoint, kOutLogProbFull>), grid, block, 0, stream, a);
+  if (mode == kOutLogProbFull) {
+    switch (route) {
+      case kRouteNone:
+        hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteNone, kOutLogProbFull>), grid, block, 0, stream, a);
+        break;
+      case kRouteTopK:
+        hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteTopK, kOutLogProbFull>), grid, block, 0, stream, a);
+        break;
+      case kRouteTopP:
+        hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteTopP, kOutLogProbFull>), grid, block, 0, stream, a);
+        break;
+      default:
+        hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteJoint, kOutLogProbFull>), grid, block, 0, stream, a);
+        break;
+    }
     return hipGetLastError();
   }
   if (mode == kOutLogProbAt) {
-    if (route == kRouteTopK)
-      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteTopK, kOutLogProbAt>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteJoint, kOutLogProbAt>), grid, block, 0, stream, a);
+    switch (route) {
+      case kRouteNone:
+        hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteNone, kOutLogProbAt>), grid, block, 0, stream, a);
+        break;
+      case kRouteTopK:
+        hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteTopK, kOutLogProbAt>), grid, block, 0, stream, a);
+        break;
+      case kRouteTopP:
+        hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteTopP, kOutLogProbAt>), grid, block, 0, stream, a);
+        break;
+      default:
+        hipLaunchKernelGGL((rows_fast_bf16_kernel<NV, kRouteJoint, kOutLogProbAt>), grid, block, 0, stream, a);
+        break;
+    }
     return hipGetLastError();
   }
   switch (route) {
@@ -1223,10 +1301,9 @@ hipError_t launch_rows(const RowArgs& a, DType dtype, Route route, OutMode mode,
     return launch_rows_topp(a, dtype, stream);
   const bool aligned = (reinterpret_cast<uintptr_t>(a.logits) % 16) == 0 && (a.row_stride % 8) == 0;
   const int64_t nvec = a.vocab / 8;
-  // the fast kernel: sampling on every route but top-p only; log-probs where
-  // top-k is on (each row without an active top-k runs the general body)
-  const bool fast_route = mode == kOutSample ? route != kRouteTopP
-                                             : (route == kRouteTopK || route == kRouteJoint);
+  // the fast kernel: sampling on every route but top-p only; log-probs on
+  // every route (rows without an active top-k write them from registers)
+  const bool fast_route = mode == kOutSample ? route != kRouteTopP : true;
   if (dtype == kBF16 && fast_route && aligned && (a.vocab % 8) == 0 && nvec <= 16 * (int64_t)kB) {
     const int64_t per = (nvec + kB - 1) / kB;
     if (per <= 1) return launch_nv<1>(a, route, mode, stream);
