@@ -612,17 +612,17 @@ __global__ __launch_bounds__(kDrawBlock) void rows_topp_draw_kernel(RowArgs a, i
   const int32_t t_end = t0 + kDrawTile < groups ? t0 + kDrawTile : groups;
   const int64_t src = a.gather ? (int64_t)a.gather[r] : (int64_t)r;
   const T* row = reinterpret_cast<const T*>(a.logits) + src * a.row_stride;
+  // the row's state through the constant address space: scalar loads
+  // (nothing this kernel writes is read this way).  Its mode first: a row
+  // already finished (greedy, +inf, nothing finite) is not read at all.
+  const __attribute__((address_space(4))) TopPRow* st =
+      (const __attribute__((address_space(4))) TopPRow*)(a.topp_rows + r);
+  if (st->mode == kTopPDone) return;             // uniform over the workgroup
 
-  // the tile's loads go out before the row's state is read
   uint32_t raw[kDrawPT][4];
 #pragma unroll
   for (int i = 0; i < kDrawPT; ++i) load_group<T, VEC>(row, v, t_end, t0 + tid + i * kDrawBlock, raw[i]);
 
-  // the row's state through the constant address space: scalar loads
-  // (nothing this kernel writes is read this way)
-  const __attribute__((address_space(4))) TopPRow* st =
-      (const __attribute__((address_space(4))) TopPRow*)(a.topp_rows + r);
-  if (st->mode == kTopPDone) return;             // uniform over the workgroup
   const float x_hi = st->x_hi;
   const float x_lo = st->x_lo;
   const float scale2 = st->scale2;
