@@ -43,6 +43,13 @@ struct alignas(16) TopPRow {
   double target;     // p times the row's mass
   double bscale;     // mass of one fixed-point unit of bucket bstar
   unsigned long long best;   // draw: max of (order of z2) << 32 | ~index over P's members
+  // log-prob calls: P = {x >= x_cut} of mass zp (set by the finish kernel);
+  // rows finished by the first kernel (kTopPDone) keep their greedy id in
+  // done_id, or -1 for a row of NaN log-probs
+  float x_cut;
+  float inv_t;       // 1 / T
+  int32_t done_id;
+  double zp;
 };
 constexpr uint32_t kTopPCut = 0;
 constexpr uint32_t kTopPDone = 1;
@@ -104,6 +111,10 @@ hipError_t launch_rows_raw_log_prob_at(const RowArgs& a, DType dtype, hipStream_
 // and a finishing kernel (one workgroup per row).
 bool topp_supported(const RowArgs& a);
 hipError_t launch_rows_topp(const RowArgs& a, DType dtype, hipStream_t stream);
+// Log-probs (full rows or at ids) of rows filtered by top-p only or not at
+// all, through the same cutoff: histogram, cutoff-bucket list, finish, and for
+// full rows a write pass.
+hipError_t launch_rows_topp_lp(const RowArgs& a, DType dtype, OutMode mode, hipStream_t stream);
 
 // The general multi-pass kernel alone (every row shape).
 hipError_t launch_rows_general(const RowArgs& a, DType dtype, Route route, OutMode mode,

@@ -1301,10 +1301,16 @@ hipError_t launch_rows(const RowArgs& a, DType dtype, Route route, OutMode mode,
     return launch_rows_topp(a, dtype, stream);
   const bool aligned = (reinterpret_cast<uintptr_t>(a.logits) % 16) == 0 && (a.row_stride % 8) == 0;
   const int64_t nvec = a.vocab / 8;
+  const bool fast_shape = dtype == kBF16 && aligned && (a.vocab % 8) == 0 && nvec <= 16 * (int64_t)kB;
+  // log-probs of rows without top-k in any other shape (fp32 above all): the
+  // top-p route's cutoff, then a write pass
+  if (mode != kOutSample && (route == kRouteTopP || route == kRouteNone) && !fast_shape &&
+      topp_supported(a))
+    return launch_rows_topp_lp(a, dtype, mode, stream);
   // the fast kernel: sampling on every route but top-p only; log-probs on
   // every route (rows without an active top-k write them from registers)
   const bool fast_route = mode == kOutSample ? route != kRouteTopP : true;
-  if (dtype == kBF16 && fast_route && aligned && (a.vocab % 8) == 0 && nvec <= 16 * (int64_t)kB) {
+  if (fast_shape && fast_route) {
     const int64_t per = (nvec + kB - 1) / kB;
     if (per <= 1) return launch_nv<1>(a, route, mode, stream);
     if (per <= 2) return launch_nv<2>(a, route, mode, stream);

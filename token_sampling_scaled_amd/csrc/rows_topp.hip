@@ -198,7 +198,7 @@ struct HistShared {
   double hit_above, hit_scale;
 };
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, int MODE>
 __global__ __launch_bounds__(kHistBlock) void rows_topp_hist_kernel(RowArgs a) {
   using E = SplitElem<T>;
   using K = typename E::Key;
@@ -263,8 +263,12 @@ __global__ __launch_bounds__(kHistBlock) void rows_topp_hist_kernel(RowArgs a) {
         }
       }
       const bool none = bj == 0x7FFFFFFF;
-      a.out_ids[r] = none ? -1 : bj;
-      if (a.out_lp) a.out_lp[r] = (none || nan_lp) ? __builtin_nanf("") : 0.0f;
+      if (MODE == kOutSample) {
+        a.out_ids[r] = none ? -1 : bj;
+        if (a.out_lp) a.out_lp[r] = (none || nan_lp) ? __builtin_nanf("") : 0.0f;
+      } else {                   // log-probs: 0 at the greedy id, or a NaN row
+        st->done_id = (none || nan_lp) ? -1 : bj;
+      }
       st->mode = kTopPDone;
     }
   };
@@ -344,8 +348,12 @@ __global__ __launch_bounds__(kHistBlock) void rows_topp_hist_kernel(RowArgs a) {
   float mrow = row_max();
   if (mrow == -__builtin_inff()) {            // no entry above -inf
     if (tid == 0) {
-      a.out_ids[r] = -1;
-      if (a.out_lp) a.out_lp[r] = __builtin_nanf("");
+      if (MODE == kOutSample) {
+        a.out_ids[r] = -1;
+        if (a.out_lp) a.out_lp[r] = __builtin_nanf("");
+      } else {
+        st->done_id = -1;
+      }
       st->mode = kTopPDone;
     }
     return;
@@ -460,6 +468,7 @@ __global__ __launch_bounds__(kHistBlock) void rows_topp_hist_kernel(RowArgs a) {
     if (tid == 0) {
       st->mode = kTopPAll;
       st->best = 0ull;
+      st->inv_t = 1.0f / temp;
       st->x_hi = kMostNegative;
       st->x_lo = kMostNegative;
       st->m0 = m0;
@@ -562,6 +571,7 @@ __global__ __launch_bounds__(kHistBlock) void rows_topp_hist_kernel(RowArgs a) {
     if (lane == 0) {
       st->mode = kTopPCut;
       st->best = 0ull;
+      st->inv_t = 1.0f / temp;
       st->bstar = bstar;
       st->x_hi = xb_hi;
       st->x_lo = xb_lo;
@@ -594,7 +604,9 @@ __global__ __launch_bounds__(kHistBlock) void rows_topp_hist_kernel(RowArgs a) {
 // x_hi) are appended to the row's list, one atomic per wave for its slots.
 // Each wave's best member goes into the row's best with one 64-bit atomic
 // maximum of (order of z2, complement of its index).
-template <typename T, bool VEC>
+// With LP (log-prob calls) only the cutoff bucket's entries are listed, for
+// the rows that have one.
+template <typename T, bool VEC, bool LP>
 __global__ __launch_bounds__(kDrawBlock) void rows_topp_draw_kernel(RowArgs a, int32_t ntiles) {
   using E = SplitElem<T>;
   using K = typename E::Key;
@@ -618,6 +630,7 @@ __global__ __launch_bounds__(kDrawBlock) void rows_topp_draw_kernel(RowArgs a, i
   const __attribute__((address_space(4))) TopPRow* st =
       (const __attribute__((address_space(4))) TopPRow*)(a.topp_rows + r);
   if (st->mode == kTopPDone) return;             // uniform over the workgroup
+  if (LP && st->mode != kTopPCut) return;
 
   uint32_t raw[kDrawPT][4];
 #pragma unroll
@@ -672,6 +685,7 @@ __global__ __launch_bounds__(kDrawBlock) void rows_topp_draw_kernel(RowArgs a, i
     }
     memm &= valid;
     bnd_any |= bndm & valid;
+    if (LP) continue;                            // no noise for log-probs
     if ((memm >> lane) & 1ull) {
       const uint32_t pos = fill + lane_rank_u64(memm);
       qg[wid][pos] = (uint32_t)g;
@@ -696,7 +710,7 @@ __global__ __launch_bounds__(kDrawBlock) void rows_topp_draw_kernel(RowArgs a, i
       }
     }
   }
-  if (fill) drain(fill);
+  if (!LP && fill) drain(fill);
 
   // the cutoff bucket's entries (a few per row): one atomic per wave
   // reserves their slots in the row's list
@@ -748,7 +762,7 @@ __global__ __launch_bounds__(kDrawBlock) void rows_topp_draw_kernel(RowArgs a, i
     const unsigned long long t = __shfl_xor(key, o, kWave);
     key = t > key ? t : key;
   }
-  if (lane == 0 && key != 0ull) atomicMax(&a.topp_rows[r].best, key);
+  if (!LP && lane == 0 && key != 0ull) atomicMax(&a.topp_rows[r].best, key);
 }
 
 // ---------------------------------------------------------------------------
@@ -760,6 +774,7 @@ struct FinShared {
   unsigned long long wtot[kFinWaves];
   double wz[kFinWaves];
   Best wbest[kFinWaves];
+  uint32_t wkmin[kFinWaves];
   int32_t hit;
   int32_t first;
   int32_t last;
@@ -864,7 +879,30 @@ __device__ __forceinline__ Best block_best(Best b, FinShared& sh) {
   return o;
 }
 
-template <typename T, bool VEC>
+// Log-prob calls (thread 0): P = {x >= x_cut} of mass zp.  At ids the entry's
+// log-prob now, (s2 - m0 - log2 zp) ln 2 as for a sampled id; full rows leave
+// the cutoff to the write kernel.
+template <typename T, int MODE>
+__device__ __forceinline__ void lp_finish(const RowArgs& a, int r, TopPRow* st, float x_cut,
+                                          double zp) {
+  using E = SplitElem<T>;
+  if (MODE == kOutLogProbAt) {
+    const int64_t j = a.token_ids[r];
+    float out = -__builtin_inff();
+    if (j >= 0 && j < a.vocab) {
+      const T* row = reinterpret_cast<const T*>(a.logits) + st->src * a.row_stride;
+      const float x = E::value(E::raw_at(row, j));
+      if (x >= x_cut)
+        out = (float)(((double)scaled2(x, st->scale2) - (double)st->m0 - log2(zp)) * 0.69314718055994531);
+    }
+    a.out_lp[r] = out;
+  } else {
+    st->x_cut = x_cut;
+    st->zp = zp;
+  }
+}
+
+template <typename T, bool VEC, int MODE>
 __global__ __launch_bounds__(kFinBlock) void rows_topp_finish_kernel(RowArgs a) {
   using E = SplitElem<T>;
   using K = typename E::Key;
@@ -875,11 +913,22 @@ __global__ __launch_bounds__(kFinBlock) void rows_topp_finish_kernel(RowArgs a) 
   const int wid = tid / kWave;
 
   // the row's state and its whole list capacity are read at once
-  const TopPRow* st = a.topp_rows + r;
+  TopPRow* st = a.topp_rows + r;
   const TopPCand mine_c = a.topp_list[(int64_t)r * kTopPListCap + tid];
   const uint32_t mode = st->mode;
-  if (mode == kTopPDone) return;
+  if (mode == kTopPDone) {
+    if (MODE == kOutLogProbAt && tid == 0) {    // 0 at the greedy id, or NaN
+      const int32_t id = st->done_id;
+      const int64_t j = a.token_ids[r];
+      a.out_lp[r] = id < 0 ? __builtin_nanf("") : (j == id ? 0.0f : -__builtin_inff());
+    }
+    return;
+  }
   const float m0 = st->m0;
+  if (MODE != kOutSample && mode == kTopPAll) {
+    if (tid == 0) lp_finish<T, MODE>(a, r, st, kMostNegative, st->above);
+    return;
+  }
   // the draw's best member (thread 0): its order word, its index, and its
   // scaled logit read back from the row
   Best tb{0u, 0x7FFFFFFF, 0.0f};
@@ -936,6 +985,29 @@ __global__ __launch_bounds__(kFinBlock) void rows_topp_finish_kernel(RowArgs a) 
     }
     const bool keep = in && (above + (double)gt * bscale < target || (above == 0.0 && gt == 0));
     double zw = keep ? (double)um * bscale : 0.0;
+    if (MODE != kOutSample) {
+      // P = everything above b* and the kept top of b*: x >= the smallest
+      // kept value (canonical keys: -0 goes with +0)
+      uint32_t kmin = keep ? mine_c.key : 0xFFFFFFFFu;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, kWave));
+      zw = wave_sum_f64(zw);
+      if (lane == 0) {
+        sh.wz[wid] = zw;
+        sh.wkmin[wid] = kmin;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        double zp = above;
+        uint32_t km = 0xFFFFFFFFu;
+        for (int w2 = 0; w2 < kFinWaves; ++w2) {
+          zp += sh.wz[w2];
+          km = min(km, sh.wkmin[w2]);
+        }
+        lp_finish<T, MODE>(a, r, st, km == 0xFFFFFFFFu ? st->x_hi : KeyRaw<T>::value_of_key(km), zp);
+      }
+      return;
+    }
     Best lb = tb;
     if (keep) {
       const float z2 = s2 + gumbel2_from_word(ns.word((uint32_t)mine_c.j));
@@ -990,6 +1062,11 @@ __global__ __launch_bounds__(kFinBlock) void rows_topp_finish_kernel(RowArgs a) 
     __syncthreads();
   }
   const uint32_t vstar = prefix;
+  if (MODE != kOutSample) {
+    if (tid == 0)
+      lp_finish<T, MODE>(a, r, st, KeyRaw<T>::value_of_key(vstar), above + (double)zp_units * bscale);
+    return;
+  }
   for_row_groups<T, VEC, kFinBlock>(row, v, groups, [&](int32_t g, const uint32_t (&raw)[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1007,12 +1084,90 @@ __global__ __launch_bounds__(kFinBlock) void rows_topp_finish_kernel(RowArgs a) 
   (void)lane;
 }
 
+// ---------------------------------------------------------------------------
+// 4. full-row log-probs: one 256-thread workgroup per (row, tile of 1024
+// groups) writes lp = x / T - (m0 + log2 zp) ln 2 on P and -inf elsewhere
+// (a greedy row: 0 at its id; a row with nothing finite: NaN).
+
+constexpr int kWriteBlock = 256;
+constexpr int kWritePT = 4;
+constexpr int kWriteTile = kWritePT * kWriteBlock;
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kWriteBlock) void rows_topp_lp_write_kernel(RowArgs a, int32_t ntiles) {
+  using E = SplitElem<T>;
+  const int r = (int)(blockIdx.x % (uint32_t)a.n);
+  const int tile = (int)(blockIdx.x / (uint32_t)a.n);
+  const int tid = threadIdx.x;
+  const int64_t v = a.vocab;
+  const int32_t groups = (int32_t)((v + 3) >> 2);
+  const int32_t t0 = tile * kWriteTile;
+  const int32_t t_end = t0 + kWriteTile < groups ? t0 + kWriteTile : groups;
+  const __attribute__((address_space(4))) TopPRow* st =
+      (const __attribute__((address_space(4))) TopPRow*)(a.topp_rows + r);
+  float* out = a.out_lp + (int64_t)r * v;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  if (st->mode == kTopPDone) {
+    const int32_t id = st->done_id;
+    for (int i = 0; i < kWritePT; ++i) {
+      const int32_t g = t0 + tid + i * kWriteBlock;
+      if (g >= t_end) break;
+      for (int e = 0; e < 4 && (int64_t)g * 4 + e < v; ++e) {
+        const int64_t j = (int64_t)g * 4 + e;
+        out[j] = id < 0 ? __builtin_nanf("") : (j == id ? 0.0f : -__builtin_inff());
+      }
+    }
+    return;
+  }
+  const int64_t src = st->src;
+  const T* row = reinterpret_cast<const T*>(a.logits) + src * a.row_stride;
+  uint32_t raw[kWritePT][4];
+#pragma unroll
+  for (int i = 0; i < kWritePT; ++i) load_group<T, VEC>(row, v, t_end, t0 + tid + i * kWriteBlock, raw[i]);
+  const float x_cut = st->x_cut;
+  const float inv_t = st->inv_t;
+  const float c0 = (float)(((double)st->m0 + log2(st->zp)) * 0.69314718055994531);
+#pragma unroll
+  for (int i = 0; i < kWritePT; ++i) {
+    const int32_t g = t0 + tid + i * kWriteBlock;
+    if (g >= t_end) continue;
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = E::value(raw[i][e]);
+      o[e] = x >= x_cut ? __builtin_fmaf(x, inv_t, -c0) : -__builtin_inff();
+    }
+    if (VEC) {
+      *reinterpret_cast<f32x4*>(out + (int64_t)g * 4) = f32x4{o[0], o[1], o[2], o[3]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((int64_t)g * 4 + e < v) out[(int64_t)g * 4 + e] = o[e];
+    }
+  }
+}
+
 template <typename T, bool VEC>
 hipError_t launch_typed(const RowArgs& a, int32_t ntiles, hipStream_t stream) {
-  hipLaunchKernelGGL((rows_topp_hist_kernel<T, VEC>), dim3(a.n), dim3(kHistBlock), 0, stream, a);
-  hipLaunchKernelGGL((rows_topp_draw_kernel<T, VEC>), dim3((uint32_t)a.n * ntiles), dim3(kDrawBlock),
+  hipLaunchKernelGGL((rows_topp_hist_kernel<T, VEC, kOutSample>), dim3(a.n), dim3(kHistBlock), 0, stream, a);
+  hipLaunchKernelGGL((rows_topp_draw_kernel<T, VEC, false>), dim3((uint32_t)a.n * ntiles), dim3(kDrawBlock),
                      0, stream, a, ntiles);
-  hipLaunchKernelGGL((rows_topp_finish_kernel<T, VEC>), dim3(a.n), dim3(kFinBlock), 0, stream, a);
+  hipLaunchKernelGGL((rows_topp_finish_kernel<T, VEC, kOutSample>), dim3(a.n), dim3(kFinBlock), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, bool VEC, int MODE>
+hipError_t launch_lp_typed(const RowArgs& a, int32_t ntiles, hipStream_t stream) {
+  hipLaunchKernelGGL((rows_topp_hist_kernel<T, VEC, MODE>), dim3(a.n), dim3(kHistBlock), 0, stream, a);
+  hipLaunchKernelGGL((rows_topp_draw_kernel<T, VEC, true>), dim3((uint32_t)a.n * ntiles), dim3(kDrawBlock),
+                     0, stream, a, ntiles);
+  hipLaunchKernelGGL((rows_topp_finish_kernel<T, VEC, MODE>), dim3(a.n), dim3(kFinBlock), 0, stream, a);
+  if (MODE == kOutLogProbFull) {
+    const int64_t groups = (a.vocab + 3) >> 2;
+    const int64_t wt = (groups + kWriteTile - 1) / kWriteTile;
+    hipLaunchKernelGGL((rows_topp_lp_write_kernel<T, VEC>), dim3((uint32_t)(a.n * wt)), dim3(kWriteBlock),
+                       0, stream, a, (int32_t)wt);
+  }
   return hipGetLastError();
 }
 
@@ -1022,6 +1177,26 @@ bool topp_supported(const RowArgs& a) {
   const int64_t groups = (a.vocab + 3) >> 2;
   const int64_t tiles = (groups + kDrawTile - 1) / kDrawTile;
   return a.topp_rows != nullptr && a.topp_list != nullptr && (int64_t)a.n * tiles < 0x7FFFFFFF;
+}
+
+hipError_t launch_rows_topp_lp(const RowArgs& a, DType dtype, OutMode mode, hipStream_t stream) {
+  if (a.n <= 0) return hipSuccess;
+  const int64_t groups = (a.vocab + 3) >> 2;
+  const int32_t ntiles = (int32_t)((groups + kDrawTile - 1) / kDrawTile);
+  const uintptr_t base = reinterpret_cast<uintptr_t>(a.logits);
+  const bool full = mode == kOutLogProbFull;
+  if (dtype == kF32) {
+    const bool vec = (base % 16) == 0 && (a.row_stride % 4) == 0 && (a.vocab % 4) == 0;
+    if (vec) return full ? launch_lp_typed<float, true, kOutLogProbFull>(a, ntiles, stream)
+                         : launch_lp_typed<float, true, kOutLogProbAt>(a, ntiles, stream);
+    return full ? launch_lp_typed<float, false, kOutLogProbFull>(a, ntiles, stream)
+                : launch_lp_typed<float, false, kOutLogProbAt>(a, ntiles, stream);
+  }
+  const bool vec = (base % 8) == 0 && (a.row_stride % 4) == 0 && (a.vocab % 4) == 0;
+  if (vec) return full ? launch_lp_typed<uint16_t, true, kOutLogProbFull>(a, ntiles, stream)
+                       : launch_lp_typed<uint16_t, true, kOutLogProbAt>(a, ntiles, stream);
+  return full ? launch_lp_typed<uint16_t, false, kOutLogProbFull>(a, ntiles, stream)
+              : launch_lp_typed<uint16_t, false, kOutLogProbAt>(a, ntiles, stream);
 }
 
 hipError_t launch_rows_topp(const RowArgs& a, DType dtype, hipStream_t stream) {
