@@ -37,6 +37,7 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "sampled rows/s + logits-read GB/s, 256x128256 bf16 top-k+top-p (% HBM peak)"
 DESCRIPTIONS = {
     "joint_128k": "256x128256 bf16 logits N(0,3^2)+spikes, per-row top-k U{1..1024} + top-p U[0.5,0.99], T U[0.5,1.5]",
+    "joint_128k_shifted": "joint_128k with row r's logits shifted by U[-16,0] before rounding to bf16",
     "topk_128k": "256x128256 bf16 logits N(0,3^2)+spikes, per-row top-k U{1..1024}, T U[0.5,1.5]",
     "none_32k": "64x32000 bf16 logits N(0,3^2), no filter",
     "topp_152k": "256x151936 fp32 Zipf(1.1) logits, per-row top-p U[0.5,0.99]",

@@ -14,6 +14,10 @@ Workloads (shapes, value laws and parameter laws):
                 positions per row (before rounding to bf16); top_k ~ U{1..1024},
                 T ~ U[0.5, 1.5]; top-k only.
   joint_128k    topk_128k's logits, k and T, plus top_p ~ U[0.5, 0.99]; joint.
+  joint_128k_shifted
+                joint_128k with row r's fp32 logits shifted by s_r ~ U[-16, 0]
+                before rounding to bf16 (the same distributions; most rows, or
+                all of their top-k, below zero).
   topp_152k     256 x 151936 fp32, x[r, perm_r(i)] = -1.1 ln i for i = 1..V
                 (Zipf(1.1) log-probabilities up to a constant, one random
                 permutation per row); T = 1, top_p ~ U[0.5, 0.99]; top-p only.
@@ -43,6 +47,7 @@ WORKLOAD_IDS = {
     "topp_152k": 4,
     "spec_mix": 5,
     "joint_128k": 6,
+    "joint_128k_shifted": 7,
 }
 
 FULL_SHAPES = {
@@ -50,6 +55,7 @@ FULL_SHAPES = {
     "none_32k": (64, 32000, torch.bfloat16),
     "topk_128k": (256, 128256, torch.bfloat16),
     "joint_128k": (256, 128256, torch.bfloat16),
+    "joint_128k_shifted": (256, 128256, torch.bfloat16),
     "topp_152k": (256, 151936, torch.float32),
     "spec_mix": (288, 128256, torch.bfloat16),
 }
@@ -122,7 +128,7 @@ def make(name: str, rows: Optional[int] = None, vocab: Optional[int] = None) -> 
                         torch.zeros(n, dtype=torch.int32), torch.ones(n, dtype=torch.float32),
                         torch.arange(n, dtype=torch.int64), no_top_k=True, no_top_p=True)
 
-    if name in ("topk_128k", "joint_128k"):
+    if name in ("topk_128k", "joint_128k", "joint_128k_shifted"):
         rng = np.random.default_rng(1000 + WORKLOAD_IDS["topk_128k"])
         x = rng.normal(0.0, 3.0, size=(n, v)).astype(np.float32)
         spikes = min(20, v)
@@ -130,11 +136,14 @@ def make(name: str, rows: Optional[int] = None, vocab: Optional[int] = None) -> 
             x[r, rng.choice(v, size=spikes, replace=False)] += np.float32(8.0)
         k = rng.integers(1, 1025, size=n).astype(np.int32)
         t = rng.uniform(0.5, 1.5, size=n).astype(np.float32)
+        if name == "joint_128k_shifted":
+            shift = np.random.default_rng(1000 + wid).uniform(-16.0, 0.0, size=n)
+            x += shift.astype(np.float32)[:, None]
         wl = Workload(name, _to_dtype(x, dtype), n, torch.from_numpy(t), torch.from_numpy(k),
                       torch.ones(n, dtype=torch.float32), torch.arange(n, dtype=torch.int64),
                       no_top_p=True)
-        if name == "joint_128k":
-            prng = np.random.default_rng(1000 + wid)
+        if name != "topk_128k":
+            prng = np.random.default_rng(1000 + WORKLOAD_IDS["joint_128k"])
             wl.top_p = torch.from_numpy(prng.uniform(0.5, 0.99, size=n).astype(np.float32))
             wl.no_top_p = False
         return wl

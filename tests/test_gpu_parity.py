@@ -20,6 +20,7 @@ SMALL = [
     ("none_32k", 16, 32000),
     ("topk_128k", 12, 20011),      # odd vocab: rows not vector aligned, ragged tail
     ("joint_128k", 12, 20000),
+    ("joint_128k_shifted", 24, 20000),   # thresholds of every sign
     ("topp_152k", 8, 30000),
     ("spec_mix", 24, 16384),
 ]
@@ -79,7 +80,8 @@ def oracle_pool():
         yield pool
 
 
-FULL = ["tiny_joint", "none_32k", "topk_128k", "joint_128k", "topp_152k", "spec_mix"]
+FULL = ["tiny_joint", "none_32k", "topk_128k", "joint_128k", "joint_128k_shifted", "topp_152k",
+        "spec_mix"]
 
 
 @pytest.mark.parametrize("name", FULL)

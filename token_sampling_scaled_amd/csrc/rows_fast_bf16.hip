@@ -69,12 +69,13 @@ struct FastShared {
   float ws[kWv];
   int32_t wj[kWv];
   uint32_t flag;                   // nonzero: the row takes the general body
+  uint32_t retry;                  // nonzero: a wave threshold <= +0 (raw patterns)
   int32_t tau_bits;                // scan results (wave 0)
   int32_t vc_bits;
   uint32_t need;
   uint32_t n_eq;
   float zp;
-  uint32_t scan_ok;
+  uint32_t scan_ok;                // 0: general body, 1: go on, 2: signed-order pass
   uint32_t nties;
   uint32_t np;
   uint32_t tmax;                   // largest wave threshold published so far
@@ -156,8 +157,49 @@ __device__ __forceinline__ int32_t elem_i16(const v4u& d, int s) {
   return (s & 1) ? hi_i16(w) : lo_i16(w);
 }
 
-// Value of a positive bf16 bit pattern.
+// Value of a bf16 bit pattern (sign-extended to 32 bits or not).
 __device__ __forceinline__ float bits_value(int32_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Signed-order patterns: a bf16 pattern read as sign and magnitude, written as
+// a two's-complement 16-bit integer (negative patterns become minus their 15
+// magnitude bits, both zeros 0), so that comparing them as signed integers is
+// the value order for every non-NaN value, with -0 and +0 equal (a positive
+// NaN above +inf, a negative one below -inf).  sord2 maps the two patterns of
+// a dword, sord16 one sign-extended pattern; sord_value16 takes one back to
+// its raw pattern (+0 for both zeros).
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t sord2(uint32_t u) {
+  const uint32_t neg = ((u >> 15) & 0x00010001u) * 0xFFFFu;   // 0xFFFF per negative half
+  const u16x2 mag = __builtin_bit_cast(u16x2, u & 0x7FFF7FFFu);
+  const uint32_t negm = __builtin_bit_cast(uint32_t, (u16x2){0, 0} - mag);   // per-half wrap
+  return (u & ~neg) | (negm & neg);
+}
+__device__ __forceinline__ v4u sord4(const v4u& v) {
+  return v4u{sord2(v.x), sord2(v.y), sord2(v.z), sord2(v.w)};
+}
+__device__ __forceinline__ int32_t sord16(int32_t b) { return b < 0 ? -(b & 0x7FFF) : b; }
+__device__ __forceinline__ int32_t sord_value16(int32_t s) { return s < 0 ? ((-s) | 0x8000) : s; }
+constexpr int32_t kNegInfOrd = -0x7F80;     // bf16 -inf in signed order
+
+// Histogram keys of signed-order patterns: the patterns of |x| < 2^-64 (a
+// biased exponent below 63, magnitude bits below kZone) share the key 0 and
+// the others close up around it, so that 32768 consecutive keys span every
+// pair of values of opposite signs that logits hold (say +1e4 down to
+// -2^114).  zkey is monotone and one-to-one outside the zone; zkey_pat takes a
+// key back to a pattern (0 for the zone), zkey_lo gives the smallest pattern
+// with a key >= c.
+constexpr int32_t kZone = 63 << 7;
+__device__ __forceinline__ int32_t zkey(int32_t s) {
+  return s >= kZone ? s - (kZone - 1) : (s <= -kZone ? s + (kZone - 1) : 0);
+}
+__device__ __forceinline__ int32_t zkey_pat(int32_t c) {
+  return c > 0 ? c + (kZone - 1) : (c < 0 ? c - (kZone - 1) : 0);
+}
+__device__ __forceinline__ int32_t zkey_lo(int32_t c) {
+  return c > 0 ? c + (kZone - 1) : c - (kZone - 1);
+}
+// Value of a pattern held raw (so false) or in signed order (so true).
+__device__ __forceinline__ float pat_value(int32_t b, bool so) { return bits_value(so ? sord_value16(b) : b); }
 
 // ---------------------------------------------------------------------------
 // wave helpers
@@ -359,12 +401,29 @@ struct ScanOut {
   float zp;           // mass of P in units of exp(x_max / T)
 };
 
-// Softmax weight exp(x / T - m) of the positive bf16 pattern b.
-__device__ __forceinline__ float bin_weight(int32_t b, float inv_t, float m) {
-  return __expf(__fmaf_rn(bits_value(b), inv_t, -m));
+// Softmax weight exp(x / T - m) of the entries of bin b: the raw pattern b
+// (so false), or the key b - hoff of signed-order patterns (so true; the
+// entries of the zone of |x| < 2^-64 weigh as x = 0, a relative change of
+// their weight below 2^-64 / T).
+__device__ __forceinline__ float bin_weight(int32_t b, float inv_t, float m, int32_t hoff, bool so) {
+  return __expf(__fmaf_rn(bits_value(so ? sord_value16(zkey_pat(b - hoff)) : b), inv_t, -m));
 }
 
-// Scan the bins [lo, hi] (bit patterns, hi = the row maximum) from the top.
+// Whether any of the bins [lo, top] of the chunk of 256 bins below top holds
+// an entry (wave-uniform).
+__device__ __forceinline__ bool chunk_any(const uint32_t* hist, int32_t top, int32_t lo, int lane) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int32_t b = top - (4 * lane + i);
+    c |= b >= lo ? hist_get(hist, b > 0 ? b : 0) : 0u;
+  }
+  return __ballot(c != 0) != 0;
+}
+
+// Scan the bins [lo, hi] (hi = the row maximum's) from the top; with so (wide
+// windows of signed-order keys, mostly empty), chunks without entries are
+// passed over.
 // Lane l takes bins top - 4l .. top - 4l - 3 of each 256-bin chunk.  When the
 // k-th value falls in the first chunk (the common case) the top-p cutoff is
 // found from the same registers; otherwise a second pass recomputes the masses.
@@ -372,7 +431,7 @@ __device__ __forceinline__ float bin_weight(int32_t b, float inv_t, float m) {
 // reaches p * Z_K; the top group is always kept.
 __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, int32_t hi,
                                              float inv_t, float m, uint32_t k, bool p_on,
-                                             float p) {
+                                             float p, int32_t hoff, bool so) {
   const int lane = threadIdx.x & (kWave - 1);
   ScanOut o{false, 0, 0, 0, 0, 0.0f};
   uint32_t cbase = 0, n_gt = 0;
@@ -381,6 +440,10 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
   uint32_t cc[4];
   float mm[4], mx[4];   // per bin: count, mass, mass of the bins above it
   for (int32_t top = hi; top >= lo; top -= 4 * kWave) {
+    if (so && !chunk_any(hist, top, lo, lane)) {   // an empty chunk: nothing to add up
+      in_first = false;
+      continue;
+    }
     uint32_t cs = 0;
     float ms = 0.0f;
 #pragma unroll
@@ -388,7 +451,7 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
       const int32_t b = top - (4 * lane + i);
       const uint32_t h = hist_get(hist, b > 0 ? b : 0);   // unconditional: the reads overlap
       cc[i] = b >= lo ? h : 0u;
-      const float w = bin_weight(b, inv_t, m);
+      const float w = bin_weight(b, inv_t, m, hoff, so);
       mm[i] = cc[i] ? (float)cc[i] * w : 0.0f;
       cs += cc[i];
       ms += mm[i];
@@ -428,7 +491,7 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
   }
   if (!o.ok) return o;
   o.need = k - n_gt;
-  const float zk = mass_gt + (float)o.need * bin_weight(o.tau_bits, inv_t, m);
+  const float zk = mass_gt + (float)o.need * bin_weight(o.tau_bits, inv_t, m, hoff, so);
   o.vc_bits = o.tau_bits;
   o.zp = zk;
   if (!p_on) return o;
@@ -456,6 +519,8 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
   }
   float mb = 0.0f;
   for (int32_t top = hi; top >= o.tau_bits; top -= 4 * kWave) {
+    // an empty chunk (the bin at tau is never empty): nothing to add up
+    if (so && !chunk_any(hist, top, o.tau_bits, lane)) continue;
     bool ne[4];
     float ms = 0.0f;
 #pragma unroll
@@ -464,7 +529,7 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
       const uint32_t h = hist_get(hist, b > 0 ? b : 0);
       const uint32_t cnt = b > o.tau_bits ? h : 0u;
       ne[i] = cnt != 0 || b == o.tau_bits;
-      const float w = bin_weight(b, inv_t, m);
+      const float w = bin_weight(b, inv_t, m, hoff, so);
       mm[i] = cnt ? (float)cnt * w : 0.0f;
       ms += mm[i];
     }
@@ -831,12 +896,26 @@ __device__ __forceinline__ int heavy_first_row(const RowArgs& a, uint64_t* cls) 
   return r >= 0 ? r : (int)blockIdx.x;   // always found: b < n and the classes split [0, n)
 }
 
-template <int NV, int ROUTE, int MODE>
-__global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
-  constexpr bool kHasK = (ROUTE == kRouteTopK || ROUTE == kRouteJoint);
-  constexpr bool kHasP = (ROUTE == kRouteTopP || ROUTE == kRouteJoint);
-  // threshold input: the first NB vectors, in groups of GV vectors (16 entries)
-  // loads in flight: the first NB vectors, then one more per arriving vector;
+// Outcome of the top-k steps: the row is done, the steps run again in signed
+// order, or the general body takes the row (after a barrier, once every wave
+// is done with the fast path's shared memory).
+constexpr int kBodyDone = 0, kBodyRetry = 1, kBodyGeneral = 2;
+
+// Steps 1-6 of a row with an active top-k (k <= kMaxK), the first NB vectors
+// of the row in d (the steps issue the other loads).  Comparisons use the bf16
+// patterns as signed 16-bit integers: raw patterns (sgn false) are in value
+// order only above +0, so in sampling mode a row with a wave threshold <= +0
+// returns true and the caller runs the steps again with sgn true, on the row
+// read again and taken to signed order (sord2) as each vector arrives.  The
+// histogram's bin of a signed-order pattern s is then zkey(s) + hoff, over the
+// 32768 keys below the row maximum's; a cut (the k-th value or the top-p
+// cutoff) in the zone of |x| < 2^-64 sends the row to the general body.  Both
+// passes stream the row the same way, so that neither needs more registers.
+template <int NV, int ROUTE, int MODE, bool sgn>
+__device__ __forceinline__ int topk_body(const RowArgs& a, int r, int64_t src, int64_t q,
+                                          const v4u* row, int nvec, int nfull, v4u (&d)[NV],
+                                          int32_t kq, float pq, bool p_on, uint64_t seed,
+                                          float inv_t, RowShared& sh) {
   // the wave threshold comes from the first NQ vectors (a quarter of the row
   // when NV >= 4), in groups of GV vectors (16 entries)
   constexpr int NB = NV >= 2 ? NV / 2 : 1;
@@ -844,69 +923,10 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   constexpr int GV = NQ >= 2 ? 2 : 1;
   constexpr int NG = NQ / GV;
   constexpr uint32_t kDiv = 8u * NV / NQ;   // c ~ 2k * (share of the row in the sample)
-  __shared__ RowShared sh;
-  __shared__ uint64_t cls[kWv];
   FastShared& fs = sh.f;
-
-  const int r = a.heavy_first ? heavy_first_row<ROUTE, MODE>(a, cls) : (int)blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wid = tid / kWave;
-  const int64_t src = a.gather ? (int64_t)a.gather[r] : (int64_t)r;
-  const int64_t q = a.req_map ? (int64_t)a.req_map[r] : (int64_t)r;
-  const v4u* row = reinterpret_cast<const v4u*>(reinterpret_cast<const uint16_t*>(a.logits) +
-                                                src * a.row_stride);
-  const int nvec = (int)(a.vocab >> 3);
-  const int nfull = nvec / kB;       // vector slots every thread of the row holds
-
-  // ---- stream the row into registers.  Slots past the row re-read its last
-  // vector and are ignored where used, so every load is unconditional and
-  // each vector is waited for on its own at its first use.  The first half is
-  // issued before the request's parameters are even read (they decide the
-  // body, and waiting for them first would delay every load by one memory
-  // latency); the second half goes out one load per arriving first-half vector.
-  v4u d[NV];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int vi = i * kB + tid;
-    d[i] = __builtin_nontemporal_load(row + (vi < nvec ? vi : nvec - 1));
-  }
-
-  const float temp = a.temperature[q];
-  const int32_t kq = kHasK ? a.top_k[q] : 0;
-  const float pq = kHasP ? a.top_p[q] : 1.0f;
-  const uint64_t seed = a.seed[q];   // read up front: a late load would stall the tail
-  const bool greedy = !(temp >= 1e-5f);
-  const bool k_on = kHasK && kq >= 1 && (int64_t)kq < a.vocab;
-  const bool p_on = kHasP && pq < 1.0f - 1e-6f;
-
-  // Rows without top-k: register-resident, below (noise for P, or the
-  // log-probs written from the registers).  k above kMaxK, and greedy rows
-  // asked for log-probs: general body.
-  const bool nok = !greedy && !k_on;
-  if ((!greedy && !nok && (!k_on || kq > kMaxK)) || (greedy && MODE != kOutSample)) {
-    general::general_row<uint16_t, ROUTE, MODE>(a, r, sh.g);
-    return;
-  }
-
-  if (greedy || nok) {
-#pragma unroll
-    for (int i = NB; i < NV; ++i) {
-      const int vi = i * kB + tid;
-      d[i] = __builtin_nontemporal_load(row + (vi < nvec ? vi : nvec - 1));
-    }
-    if (greedy) {
-      greedy_row<NV>(a, r, nvec, d, fs);
-      return;
-    }
-    if (!nok_row<NV, MODE>(a, r, nvec, nfull, d, 1.0f / temp, p_on, pq, seed, noise_offset(a, q), sh)) {
-      __syncthreads();
-      general::general_row<uint16_t, ROUTE, MODE>(a, r, sh.g);
-    }
-    return;
-  }
-  const float inv_t = 1.0f / temp;
-
   // clear the histogram while the loads are in flight
   {
     v4u* h4 = reinterpret_cast<v4u*>(fs.hist);
@@ -914,6 +934,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
     for (int i = 0; i < kHistBins / 8 / kB; ++i) h4[i * kB + tid] = v4u{0u, 0u, 0u, 0u};
     if (tid == 0) {
       fs.flag = 0;
+      fs.retry = 0;
       fs.nties = 0;
       fs.np = 0;
       fs.tmax = 0;
@@ -927,6 +948,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   int32_t vm[NQ];
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
+    if constexpr (sgn) d[i] = sord4(d[i]);
     vm[i] = (i < nfull || tid < nvec - i * kB) ? vec_max_i16(d[i]) : -32768;
     vmax = max(vmax, vm[i]);
     if (NB + i < NV) {
@@ -947,12 +969,21 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   const uint32_t cq = ((uint32_t)kq + kDiv - 1) / kDiv + 4;
   const uint32_t c = (uint32_t)kq < cq ? (uint32_t)kq : cq;
   const uint32_t tw = wave_cth_largest16<NG>(gm, c);
-  const bool wave_ok = (int32_t)tw - 0x8000 > 0;   // the signed order is the value order only above +0
+  // raw patterns: the signed order is the value order only above +0.  Signed
+  // order: the threshold must lie above -inf (so that no -inf or NaN entry can
+  // be counted).
+  const int32_t t16w = (int32_t)tw - 0x8000;
+  const bool wave_ok = tw != 0 && (sgn ? t16w > kNegInfOrd : t16w > 0);
   // t* = max_w t_w is where the scan stops, so an entry below the largest
   // threshold published so far can never matter: filter with that one
   uint32_t teff = tw;
   if (lane == 0) {
-    if (!wave_ok) fs.flag = 1;
+    if (!wave_ok) {
+      // log-prob rows keep the row in registers through the steps, which two
+      // instances of them cannot afford without spills: general body
+      if (!sgn && tw != 0 && MODE == kOutSample) fs.retry = 1;
+      else fs.flag = 1;
+    }
     if (wave_ok) teff = max(tw, atomicMax(&fs.tmax, tw));
   }
   teff = (uint32_t)__builtin_amdgcn_readfirstlane((int)teff);
@@ -982,6 +1013,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
     for (int i = 0; i < NQ; ++i) offer(i, vm[i]);
 #pragma unroll
     for (int i = NQ; i < NV; ++i) {
+      if constexpr (sgn) d[i] = sord4(d[i]);
       const int32_t mv = (i < nfull || tid < nvec - i * kB) ? vec_max_i16(d[i]) : -32768;
       vmax = max(vmax, mv);
       if (i < NB && NB + i < NV) {
@@ -995,11 +1027,21 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   }
   if (lane == 0 && wfill > (uint32_t)kSegV) fs.flag = 1;   // a full segment lost vectors
   const uint32_t stored = wfill < (uint32_t)kSegV ? wfill : (uint32_t)kSegV;
+  // signed order: the row maximum places the histogram's window before any
+  // entry is counted, and nothing below the window is
+  int32_t hoff = 0, tlo = -32768;
+  if constexpr (sgn) {
+    const uint32_t wmaxu = wave_max_dpp((uint32_t)(vmax + 0x8000));
+    if (lane == 0) atomicMax(&fs.kmax, wmaxu);
+    __syncthreads();
+    hoff = 0x7FFF - zkey((int32_t)fs.kmax - 0x8000);
+    tlo = zkey_lo(-hoff);
+  }
   {
     // entries >= the largest threshold published by now (<= t*) go into the
     // histogram; stored vectors whose maximum is below it are skipped
     wave_lds_sync();
-    const int32_t tc = max(t16, (int32_t)fs.tmax - 0x8000);
+    const int32_t tc = max(max(t16, (int32_t)fs.tmax - 0x8000), tlo);
     const i16x2 tc2 = __builtin_bit_cast(i16x2, (uint32_t)tc * 0x10001u);
     for (uint32_t e = lane; e < stored; e += kWave) {
       const int32_t vmx = (int32_t)my_vim[e] >> 16;
@@ -1012,12 +1054,12 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
         nlt += (uint32_t)__popc(__builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(
                                     __builtin_bit_cast(i16x2, word_of(dv, w)), tc2)) & 0x80008000u);
       if (nlt == 7) {                // the maximum is the only entry >= tc
-        hist_add(fs.hist, vmx);
+        hist_add(fs.hist, sgn ? zkey(vmx) + hoff : vmx);
       } else {
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
           const int32_t val = elem_i16(dv, s);
-          if (val >= tc) hist_add(fs.hist, val);
+          if (val >= tc) hist_add(fs.hist, sgn ? zkey(val) + hoff : val);
         }
       }
     }
@@ -1039,12 +1081,24 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
     const uint32_t tstaru = fs.tmax;
     const int32_t kmax16 = (int32_t)kmaxu - 0x8000;
     const int32_t tstar16 = (int32_t)tstaru - 0x8000;
-    m = __fmul_rn(bits_value(kmax16), inv_t);
-    const bool usable = fs.flag == 0 && kmax16 <= kPosInfBits;   // no NaN, no full segment
+    m = __fmul_rn(pat_value(kmax16, sgn), inv_t);
+    // a wave threshold <= +0 (raw patterns, sampling): signed-order pass
+    const bool retry = MODE == kOutSample && !sgn && fs.retry != 0;
+    const bool usable = !retry && fs.flag == 0 && kmax16 <= kPosInfBits;   // no NaN, no full segment
     ScanOut so{false, 0, 0, 0, 0, 0.0f};
-    if (usable) so = scan_hist(fs.hist, tstar16, kmax16, inv_t, m, (uint32_t)kq, p_on, pq);
+    if (usable) {
+      const int32_t lo = sgn ? max(zkey(tstar16), -hoff) + hoff : tstar16;
+      const int32_t hi = sgn ? zkey(kmax16) + hoff : kmax16;
+      so = scan_hist(fs.hist, lo, hi, inv_t, m, (uint32_t)kq, p_on, pq, hoff, sgn);
+      if constexpr (sgn) {
+        // keys back to patterns; a cut in the zone has no exact pattern
+        if (so.tau_bits == hoff || so.vc_bits == hoff) so.ok = false;
+        so.tau_bits = zkey_pat(so.tau_bits - hoff);
+        so.vc_bits = zkey_pat(so.vc_bits - hoff);
+      }
+    }
     if (lane == 0) {
-      fs.scan_ok = so.ok ? 1u : 0u;
+      fs.scan_ok = retry ? 2u : so.ok ? 1u : 0u;
       fs.tau_bits = so.tau_bits;
       fs.vc_bits = so.vc_bits;
       fs.need = so.need;
@@ -1054,11 +1108,8 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
     }
   }
   __syncthreads();
-  if (fs.scan_ok == 0) {
-    __syncthreads();
-    general::general_row<uint16_t, ROUTE, MODE>(a, r, sh.g);
-    return;
-  }
+  const uint32_t scan_ok = fs.scan_ok;
+  if (scan_ok != 1u) return (MODE == kOutSample && !sgn && scan_ok == 2u) ? kBodyRetry : kBodyGeneral;
   const int32_t tau = fs.tau_bits;
   const int32_t vc = fs.vc_bits;
   const uint32_t need = fs.need;
@@ -1087,9 +1138,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
       __syncthreads();
       nt = fs.nties;
       if (nt > (uint32_t)kMaxTies) {
-        __syncthreads();
-        general::general_row<uint16_t, ROUTE, MODE>(a, r, sh.g);
-        return;
+        return kBodyGeneral;
       }
     }
     const float mrow = fs.mrow;
@@ -1098,7 +1147,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
     auto lp_of = [&](int32_t val, uint32_t j) -> float {
       bool keep = val >= thr;
       if (tie_cut && val == tau) keep = tie_rank(fs.ties, nt, j) < need;
-      return keep ? __fmul_rn(bits_value(val), inv_t) - mrow - lzp : -__builtin_inff();
+      return keep ? __fmul_rn(pat_value(val, sgn), inv_t) - mrow - lzp : -__builtin_inff();
     };
     if (MODE == kOutLogProbAt) {
       if (tid == 0) {
@@ -1106,11 +1155,12 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
         float out = -__builtin_inff();
         if (j >= 0 && j < a.vocab) {
           const uint16_t raw = reinterpret_cast<const uint16_t*>(a.logits)[src * a.row_stride + j];
-          out = lp_of((int32_t)(int16_t)raw, (uint32_t)j);
+          const int32_t pat = (int32_t)(int16_t)raw;
+          out = lp_of(sgn ? sord16(pat) : pat, (uint32_t)j);
         }
         a.out_lp[r] = out;
       }
-      return;
+      return kBodyDone;
     }
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     f32x4* out_row = reinterpret_cast<f32x4*>(a.out_lp + (int64_t)r * a.vocab);
@@ -1128,7 +1178,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
       out_row[2 * vi] = f32x4{o[0], o[1], o[2], o[3]};
       out_row[2 * vi + 1] = f32x4{o[4], o[5], o[6], o[7]};
     }
-    return;
+    return kBodyDone;
   }
   const uint64_t off = noise_offset(a, q);
   const NoiseStream ns{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
@@ -1184,9 +1234,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   const uint32_t nmv = fs.np;
   const uint32_t nt = tie_cut ? fs.nties : 0u;
   if (nmv > (uint32_t)kMaxK || nt > (uint32_t)kMaxTies) {
-    __syncthreads();
-    general::general_row<uint16_t, ROUTE, MODE>(a, r, sh.g);
-    return;
+    return kBodyGeneral;
   }
 
   // ---- 5. one listed vector per thread: its members (x >= thr outright; of
@@ -1194,7 +1242,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   // draw their noise.  At most 64 listed vectors: wave 0 alone, else every
   // wave and a block argmax.
   const bool one_wave = nmv <= (uint32_t)kWave;
-  if (one_wave && wid != 0) return;
+  if (one_wave && wid != 0) return kBodyDone;
   const int32_t thr = tie_cut ? tau + 1 : vc;
   const int32_t eqv = tie_cut ? tau : 0x7FFFFFFF;
   Pick best{-__builtin_inff(), 0x7FFFFFFF, 0.0f};
@@ -1220,7 +1268,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
       const int sl = __ffs(mk) - 1;
       mk &= mk - 1;
       const uint32_t j = vi * 8 + (uint32_t)sl;
-      const float sv = __fmul_rn(bits_value(elem_i16(dv, sl)), inv_t);
+      const float sv = __fmul_rn(pat_value(elem_i16(dv, sl), sgn), inv_t);
       const float z = sv + gumbel_from_word(ns.word(j));
       if (z > best.z || (z == best.z && (int32_t)j < best.j)) best = Pick{z, (int32_t)j, sv};
     }
@@ -1228,10 +1276,93 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   if (one_wave) {
     best = wave_pick(best);
     if (lane == 0) write_result(a, r, best.j, best.s - m - __logf(fs.zp));
-    return;
+    return kBodyDone;
   }
   best = block_pick(best, fs);
   if (tid == 0) write_result(a, r, best.j, best.s - m - __logf(fs.zp));
+  return kBodyDone;
+}
+
+template <int NV, int ROUTE, int MODE>
+__global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
+  constexpr bool kHasK = (ROUTE == kRouteTopK || ROUTE == kRouteJoint);
+  constexpr bool kHasP = (ROUTE == kRouteTopP || ROUTE == kRouteJoint);
+  // loads in flight: the first NB vectors, then (in the steps) one more per
+  // arriving vector
+  constexpr int NB = NV >= 2 ? NV / 2 : 1;
+  __shared__ RowShared sh;
+  __shared__ uint64_t cls[kWv];
+  FastShared& fs = sh.f;
+
+  const int r = a.heavy_first ? heavy_first_row<ROUTE, MODE>(a, cls) : (int)blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t src = a.gather ? (int64_t)a.gather[r] : (int64_t)r;
+  const int64_t q = a.req_map ? (int64_t)a.req_map[r] : (int64_t)r;
+  const v4u* row = reinterpret_cast<const v4u*>(reinterpret_cast<const uint16_t*>(a.logits) +
+                                                src * a.row_stride);
+  const int nvec = (int)(a.vocab >> 3);
+  const int nfull = nvec / kB;       // vector slots every thread of the row holds
+
+  // ---- stream the row into registers.  Slots past the row re-read its last
+  // vector and are ignored where used, so every load is unconditional and
+  // each vector is waited for on its own at its first use.  The first half is
+  // issued before the request's parameters are even read (they decide the
+  // body, and waiting for them first would delay every load by one memory
+  // latency); the second half goes out one load per arriving first-half vector.
+  v4u d[NV];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int vi = i * kB + tid;
+    d[i] = __builtin_nontemporal_load(row + (vi < nvec ? vi : nvec - 1));
+  }
+
+  const float temp = a.temperature[q];
+  const int32_t kq = kHasK ? a.top_k[q] : 0;
+  const float pq = kHasP ? a.top_p[q] : 1.0f;
+  const uint64_t seed = a.seed[q];   // read up front: a late load would stall the tail
+  const bool greedy = !(temp >= 1e-5f);
+  const bool k_on = kHasK && kq >= 1 && (int64_t)kq < a.vocab;
+  const bool p_on = kHasP && pq < 1.0f - 1e-6f;
+
+  // Rows without top-k: register-resident, below (noise for P, or the
+  // log-probs written from the registers).  k above kMaxK, and greedy rows
+  // asked for log-probs: general body.
+  const bool nok = !greedy && !k_on;
+  int st = kBodyGeneral;             // uniform over the workgroup
+  if ((!greedy && !nok && (!k_on || kq > kMaxK)) || (greedy && MODE != kOutSample)) {
+    // general body from the start
+  } else if (greedy || nok) {
+#pragma unroll
+    for (int i = NB; i < NV; ++i) {
+      const int vi = i * kB + tid;
+      d[i] = __builtin_nontemporal_load(row + (vi < nvec ? vi : nvec - 1));
+    }
+    if (greedy) {
+      greedy_row<NV>(a, r, nvec, d, fs);
+      st = kBodyDone;
+    } else {
+      st = nok_row<NV, MODE>(a, r, nvec, nfull, d, 1.0f / temp, p_on, pq, seed, noise_offset(a, q), sh)
+               ? kBodyDone : kBodyGeneral;
+    }
+  } else {
+    const float inv_t = 1.0f / temp;
+    st = topk_body<NV, ROUTE, MODE, false>(a, r, src, q, row, nvec, nfull, d, kq, pq, p_on, seed,
+                                           inv_t, sh);
+    if (MODE == kOutSample && st == kBodyRetry) {
+      // a wave threshold <= +0: the steps again, in signed order, on the row read again
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int vi = i * kB + tid;
+        d[i] = __builtin_nontemporal_load(row + (vi < nvec ? vi : nvec - 1));
+      }
+      st = topk_body<NV, ROUTE, MODE, true>(a, r, src, q, row, nvec, nfull, d, kq, pq, p_on, seed,
+                                            inv_t, sh);
+    }
+  }
+  if (st == kBodyGeneral) {
+    __syncthreads();
+    general::general_row<uint16_t, ROUTE, MODE>(a, r, sh.g);
+  }
 }
 
 template <int NV>
