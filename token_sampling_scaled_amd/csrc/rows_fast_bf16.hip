@@ -91,6 +91,9 @@ struct NoKShared {
   uint32_t wkey[kWv];
   uint32_t wnan[kWv];              // lanes of the wave holding a negative NaN
   float wz[kWv];
+  float wpz[kWv];                  // per-wave race winners (no-filter rows)
+  int32_t wpj[kWv];
+  float wps[kWv];
   uint32_t vc_key;                 // the cutoff group's order key
   float zp;                        // mass of P in units of exp(x_max / T)
   uint32_t ok;                     // 0: the cutoff lies below the window
@@ -658,6 +661,68 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
   const float m2 = key_value(kmx) * sc2;
   const float m = __fmul_rn(key_value(kmx), inv_t);
 
+  if (MODE == kOutSample && !p_on) {
+    // ---- P = every finite entry: Z and the perturbed argmax in one pass.
+    // argmax_j (x_j / T + g_j), g_j = -ln(-ln u_j), is the winner of an
+    // exponential race: argmin_j E_j / w_j with w_j = exp2(s2_j - m2) (the
+    // terms of Z) and E_j = -log2 u_j (-ln u_j times log2 e, one factor for
+    // every j).  j beats the best b so far when E_j w_b < E_b w_j: no
+    // division, and one logarithm per entry besides the exp2 Z needs anyway.
+    // -inf entries weigh 0 and never win.  Z adds the same terms in the same
+    // order as the two-pass form below.
+    const NoiseStream nst{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
+                          (uint32_t)off, (uint32_t)(off >> 32)};
+    float z = 0.0f, eb = 1.0f, wb = 0.0f, xb = 0.0f;
+    int32_t jb = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int vi = i * kB + tid;
+      if (!(i < nfull || vi < nvec)) continue;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const Philox4 wds = nst.block((uint32_t)(2 * vi + h));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t u = word_of(d[i], 2 * h + (e >> 1));
+          const float x = __uint_as_float((e & 1) ? (u & 0xFFFF0000u) : (u << 16));
+          const float w = __builtin_amdgcn_exp2f(__fmaf_rn(x, sc2, -m2));
+          z += w;
+          const float ee = -__builtin_amdgcn_logf(uniform_from_word(wds.v[e]));
+          if (ee * wb < eb * w) {          // j rises within a thread: ties keep the first
+            eb = ee;
+            wb = w;
+            xb = x;
+            jb = vi * 8 + 4 * h + e;
+          }
+        }
+      }
+    }
+    // the thread's winner as a base-2 score log2 w - log2 E (w > 0: the row
+    // holds a finite entry, which weighs at least as much as exp2(0) = 1 at
+    // its maximum, so some thread's wb is positive; a thread with none keeps -inf)
+    Pick p{wb > 0.0f ? __builtin_amdgcn_logf(wb) - __builtin_amdgcn_logf(eb) : -__builtin_inff(), jb,
+           __fmul_rn(xb, inv_t)};
+    z = wave_sum(z);
+    p = wave_pick(p);
+    if (lane == 0) {
+      ns_.wz[wid] = z;
+      ns_.wpz[wid] = p.z;
+      ns_.wpj[wid] = p.j;
+      ns_.wps[wid] = p.s;
+    }
+    __syncthreads();
+    if (wid == 0) {
+      float zt = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWv; ++w) zt += ns_.wz[w];
+      Pick b{-__builtin_inff(), 0x7FFFFFFF, 0.0f};
+      if (lane < kWv) b = Pick{ns_.wpz[lane], ns_.wpj[lane], ns_.wps[lane]};
+      b = wave_pick(b);
+      if (lane == 0) write_result(a, r, b.j, b.s - m - __logf(zt));
+    }
+    return true;
+  }
+
   // ---- Z = sum over finite entries of exp(x / T - m) (exp2 of -inf is 0)
   float z = 0.0f;
 #pragma unroll
@@ -769,7 +834,6 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
   // the members of P: canonical key >= vc_key, that is raw key >= raw_thr
   // (-0 too when the cutoff group is +0's)
   const uint32_t raw_thr = vc_key == kPosZeroKey ? kNegZeroKey : vc_key;
-  const uint32_t below_m = (raw_thr - 1u) * 0x10001u;
   if (MODE != kOutSample) {
     // lp = x / T - m - ln Z_P on P, -inf elsewhere
     const float lzp = __logf(zp);
@@ -809,7 +873,10 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
     return true;
   }
 
-  // ---- Philox noise for the members of P, perturbed argmax
+  // ---- Philox noise for the members of P (x at or above the cutoff group's
+  // value: -0 with +0, never -inf), perturbed argmax.  A lane whose block of
+  // four entries holds no member skips its Philox block.
+  const float x_thr = key_value(vc_key);
   const NoiseStream nst{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
                         (uint32_t)off, (uint32_t)(off >> 32)};
   Pick best{-__builtin_inff(), 0x7FFFFFFF, 0.0f};
@@ -820,20 +887,16 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       // entries 4h .. 4h + 3 of the vector: one Philox block
-      const uint32_t k2a = keys2(word_of(d[i], 2 * h));
-      const uint32_t k2b = keys2(word_of(d[i], 2 * h + 1));
-      const uint32_t ha = pk_sub_sat_u16(k2a, below_m);
-      const uint32_t hb = pk_sub_sat_u16(k2b, below_m);
-      if ((ha | hb) == 0) continue;
-      const uint32_t kk[4] = {k2a & 0xFFFFu, k2a >> 16, k2b & 0xFFFFu, k2b >> 16};
-      const bool mem[4] = {(ha & 0xFFFFu) != 0, (ha >> 16) != 0, (hb & 0xFFFFu) != 0, (hb >> 16) != 0};
+      const uint32_t ua = word_of(d[i], 2 * h), ub = word_of(d[i], 2 * h + 1);
+      const float x[4] = {__uint_as_float(ua << 16), __uint_as_float(ua & 0xFFFF0000u),
+                          __uint_as_float(ub << 16), __uint_as_float(ub & 0xFFFF0000u)};
+      if (!(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])) >= x_thr)) continue;
       const Philox4 wds = nst.block((uint32_t)(2 * vi + h));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (!mem[e]) continue;
-        const float sv = __fmul_rn(key_value(kk[e]), inv_t);
+        const float sv = __fmul_rn(x[e], inv_t);
         const float zz = sv + gumbel_from_word(wds.v[e]);
-        if (zz > best.z) best = Pick{zz, vi * 8 + 4 * h + e, sv};   // j rises within a thread
+        if (x[e] >= x_thr && zz > best.z) best = Pick{zz, vi * 8 + 4 * h + e, sv};   // j rises within a thread
       }
     }
   }
