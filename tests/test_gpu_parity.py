@@ -302,6 +302,41 @@ def test_bf16_like_ties_and_misaligned_stride(dtype):
         _run_custom(wl)
 
 
+def _small_f32_rows(v, seed):
+    """fp32 rows for the short-row kernel: heavy ties, signed zeros, -inf and
+    NaN sprinkled in, one row with fewer finite entries than most k, one flat
+    row (a single histogram bin: more candidates than the kernel keeps, so the
+    general body) and one of coarse ties (large tie groups at the cut)."""
+    rng = np.random.default_rng(seed)
+    rows = np.round(rng.normal(0, 2, size=(8, v)) * 8) / 8
+    rows[1, rng.choice(v, v // 8, replace=False)] = -np.inf
+    rows[1, rng.choice(v, 9, replace=False)] = np.nan
+    rows[2, : v // 2] = -0.0
+    rows[2, v // 2:] = 0.0
+    rows[2, rng.choice(v, 40, replace=False)] = rng.normal(0, 1, 40)
+    rows[3, :] = -np.inf
+    rows[3, rng.choice(v, 30, replace=False)] = rng.normal(0, 1, 30)
+    rows[4, :] = 1.5
+    rows[5] = np.round(rows[5])
+    rows[6] -= 30.0
+    return rows
+
+
+@pytest.mark.parametrize("v", [4096, 8192])
+@pytest.mark.parametrize("k,p,t", [(1, 1.0, 1.0), (50, 0.9, 0.7), (256, 0.95, 1.3), (257, 0.9, 1.0),
+                                   (50, 1.0, 0.0), (200, 0.3, 0.5)])
+def test_short_fp32_rows_with_top_k(v, k, p, t):
+    """The register-resident fp32 kernel for short rows (joint and top-k routes),
+    with the rows it hands to the general body (k above 256, greedy, +inf, more
+    than 1024 candidates, nothing finite)."""
+    rows = _small_f32_rows(v, 100 + k)
+    wl = _custom(rows, torch.float32, k=k, p=p, t=t)
+    print(f"[case] short fp32 v={v} k={k} p={p} t={t}", flush=True)
+    _run_custom(wl)
+    wl = _custom(rows, torch.float32, k=k, p=p, t=t, stride_pad=4)   # padded rows, still aligned
+    _run_custom(wl)
+
+
 def test_determinism_and_step_offset():
     wl = synth.make("spec_mix", rows=24, vocab=16384)
     dev = parity.to_device(wl)

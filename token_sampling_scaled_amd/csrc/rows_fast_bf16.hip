@@ -207,58 +207,8 @@ __device__ __forceinline__ float pat_value(int32_t b, bool so) { return bits_val
 // ---------------------------------------------------------------------------
 // wave helpers
 
-// Inclusive prefix sum over the 64 lanes: DPP row shifts inside each row of 16
-// lanes, then row broadcasts of lanes 15 and 31.
-__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v) {
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
-  return v;
-}
-
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(
-      __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xF, false));
-}
-
-__device__ __forceinline__ float wave_scan_f32(float v) {
-  v += dpp_f<0x111, 0xF>(v);
-  v += dpp_f<0x112, 0xF>(v);
-  v += dpp_f<0x114, 0xF>(v);
-  v += dpp_f<0x118, 0xF>(v);
-  v += dpp_f<0x142, 0xA>(v);
-  v += dpp_f<0x143, 0xC>(v);
-  return v;
-}
-
 __device__ __forceinline__ uint32_t lane_rank(unsigned long long m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-// Wave-wide max / min (result in every lane): DPP row shifts, row broadcasts,
-// then the last lane's value.
-__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
-}
-
-__device__ __forceinline__ uint32_t wave_min_dpp(uint32_t v) {
-  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x111, 0xF, 0xF, false));
-  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x112, 0xF, 0xF, false));
-  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x114, 0xF, 0xF, false));
-  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x118, 0xF, 0xF, false));
-  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x142, 0xA, 0xF, false));
-  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x143, 0xC, 0xF, false));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
 
 // c-th largest (c >= 1) of the wave's values, 0 standing for "no value" (the
@@ -296,16 +246,6 @@ struct Pick {
   float s;
 };
 
-__device__ __forceinline__ float wave_max_f32_dpp(float v) {
-  constexpr int kNegInf = (int)0xFF800000u;
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(v), 0x111, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(v), 0x112, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(v), 0x114, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(v), 0x118, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(v), 0x142, 0xA, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(v), 0x143, 0xC, 0xF, false)));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
-}
 
 // Best (largest z, then smallest j) of the wave, returned in every lane.
 __device__ __forceinline__ Pick wave_pick(Pick p) {
@@ -1512,6 +1452,8 @@ hipError_t launch_rows(const RowArgs& a, DType dtype, Route route, OutMode mode,
     if (per <= 8) return launch_nv<8>(a, route, mode, stream);
     return launch_nv<16>(a, route, mode, stream);
   }
+  // short fp32 rows with top-k: their own register-resident kernel
+  if (small_f32_supported(a, dtype, route, mode)) return launch_rows_small_f32(a, route, stream);
   return launch_rows_general(a, dtype, route, mode, stream);
 }
 
