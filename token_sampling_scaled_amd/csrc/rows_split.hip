@@ -174,6 +174,13 @@ __global__ __launch_bounds__(kSplitBlock) void rows_split_none_kernel(RowArgs a,
     // seen every other bump, so every partial has landed, and it reads them
     // back with device-coherent loads.  (A release / acquire pair would also
     // write back and invalidate whole L2 caches on every workgroup.)
+    // Basis: the GFX942/GFX950 memory model of the LLVM AMDGPU backend
+    // (AMDGPUUsage, "Memory Model GFX942"): agent-scope atomic stores and
+    // loads are sc1 accesses that reach the coherence point past the per-XCD
+    // L2, and an agent-scope release is an L2 write-back plus s_waitcnt
+    // vmcnt(0).  The write-back only matters for ordinary stores; the
+    // partial has none, so the wait alone orders its stores before the
+    // ticket.
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     sticket = __hip_atomic_fetch_add(a.split_counter + r, 1u, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
