@@ -302,6 +302,34 @@ def test_bf16_like_ties_and_misaligned_stride(dtype):
         _run_custom(wl)
 
 
+def _signed_bf16_rows(v, seed):
+    """bf16 rows whose top-k cut is at or below zero: all negative, crossing
+    zero, signed zeros at the cut, and values inside |x| < 2^-64 (the zone the
+    register-resident kernel's second pass cannot cut in: general body)."""
+    rng = np.random.default_rng(seed)
+    rows = np.empty((6, v), dtype=np.float32)
+    rows[0] = rng.normal(-20.0, 3.0, v)
+    rows[1] = rng.normal(0.0, 1.0, v)
+    rows[2] = np.where(rng.random(v) < 0.5, -0.0, 0.0)
+    rows[2, rng.choice(v, 20, replace=False)] = rng.normal(2.0, 1.0, 20)
+    rows[3] = rng.normal(0.0, 1.0, v) * 1e-25
+    rows[4] = rng.normal(-3.0, 2.0, v)
+    rows[4, rng.choice(v, 5, replace=False)] = 6.0
+    rows[5] = -rng.exponential(1.0, v)
+    return rows
+
+
+@pytest.mark.parametrize("k,p,t", [(1, 1.0, 1.0), (60, 0.9, 0.8), (700, 0.95, 1.2), (1024, 1.0, 1.0),
+                                   (2500, 0.5, 1.0)])
+def test_bf16_rows_cut_at_or_below_zero(k, p, t):
+    """The signed-order second pass of the register-resident kernel (and the
+    rows it sends on to the general body)."""
+    rows = _signed_bf16_rows(4096, 7 + k)
+    wl = _custom(rows, torch.bfloat16, k=k, p=p, t=t)
+    print(f"[case] signed bf16 k={k} p={p} t={t}", flush=True)
+    _run_custom(wl)
+
+
 def _small_f32_rows(v, seed):
     """fp32 rows for the short-row kernel: heavy ties, signed zeros, -inf and
     NaN sprinkled in, one row with fewer finite entries than most k, one flat
