@@ -899,6 +899,13 @@ __device__ __forceinline__ int heavy_first_row(const RowArgs& a, uint64_t* cls) 
   return r >= 0 ? r : (int)blockIdx.x;   // always found: b < n and the classes split [0, n)
 }
 
+// Whether a row with a wave threshold at or below +0 takes the signed-order
+// second pass (else the general body): every instance but full-row log-probs
+// on the joint route at 16 vectors a thread, where a second copy of the steps
+// beside the register-resident row makes the first copy spill.
+template <int NV, int ROUTE, int MODE>
+constexpr bool kSignedPass = !(MODE == kOutLogProbFull && ROUTE == kRouteJoint && NV == 16);
+
 // Outcome of the top-k steps: the row is done, the steps run again in signed
 // order, or the general body takes the row (after a barrier, once every wave
 // is done with the fast path's shared memory).
@@ -982,9 +989,7 @@ __device__ __forceinline__ int topk_body(const RowArgs& a, int r, int64_t src, i
   uint32_t teff = tw;
   if (lane == 0) {
     if (!wave_ok) {
-      // log-prob rows keep the row in registers through the steps, which two
-      // instances of them cannot afford without spills: general body
-      if (!sgn && tw != 0 && MODE == kOutSample) fs.retry = 1;
+      if (!sgn && tw != 0 && kSignedPass<NV, ROUTE, MODE>) fs.retry = 1;
       else fs.flag = 1;
     }
     if (wave_ok) teff = max(tw, atomicMax(&fs.tmax, tw));
@@ -1086,7 +1091,7 @@ __device__ __forceinline__ int topk_body(const RowArgs& a, int r, int64_t src, i
     const int32_t tstar16 = (int32_t)tstaru - 0x8000;
     m = __fmul_rn(pat_value(kmax16, sgn), inv_t);
     // a wave threshold <= +0 (raw patterns, sampling): signed-order pass
-    const bool retry = MODE == kOutSample && !sgn && fs.retry != 0;
+    const bool retry = kSignedPass<NV, ROUTE, MODE> && !sgn && fs.retry != 0;
     const bool usable = !retry && fs.flag == 0 && kmax16 <= kPosInfBits;   // no NaN, no full segment
     ScanOut so{false, 0, 0, 0, 0, 0.0f};
     if (usable) {
@@ -1112,7 +1117,8 @@ __device__ __forceinline__ int topk_body(const RowArgs& a, int r, int64_t src, i
   }
   __syncthreads();
   const uint32_t scan_ok = fs.scan_ok;
-  if (scan_ok != 1u) return (MODE == kOutSample && !sgn && scan_ok == 2u) ? kBodyRetry : kBodyGeneral;
+  if (scan_ok != 1u)
+    return (kSignedPass<NV, ROUTE, MODE> && !sgn && scan_ok == 2u) ? kBodyRetry : kBodyGeneral;
   const int32_t tau = fs.tau_bits;
   const int32_t vc = fs.vc_bits;
   const uint32_t need = fs.need;
@@ -1172,8 +1178,13 @@ __device__ __forceinline__ int topk_body(const RowArgs& a, int r, int64_t src, i
       const int vi = i * kB + tid;
       if (!(i < nfull || vi < nvec)) continue;
       float o[8];
+      // the second pass reads its row a third time here rather than keep it
+      // in registers through the steps (a second register-resident copy of
+      // them does not fit without spills)
+      v4u dv = d[i];
+      if constexpr (sgn) dv = sord4(__builtin_nontemporal_load(row + vi));
 #pragma unroll
-      for (int sl = 0; sl < 8; ++sl) o[sl] = lp_of(elem_i16(d[i], sl), (uint32_t)(vi * 8 + sl));
+      for (int sl = 0; sl < 8; ++sl) o[sl] = lp_of(elem_i16(dv, sl), (uint32_t)(vi * 8 + sl));
       // plain stores: each of the two lands at a 32-byte stride, and the L2
       // merges both halves of every line before it goes to HBM (non-temporal
       // stores leave half-filled lines: 68 us instead of 39 us per call at
@@ -1351,7 +1362,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
     const float inv_t = 1.0f / temp;
     st = topk_body<NV, ROUTE, MODE, false>(a, r, src, q, row, nvec, nfull, d, kq, pq, p_on, seed,
                                            inv_t, sh);
-    if (MODE == kOutSample && st == kBodyRetry) {
+    if (kSignedPass<NV, ROUTE, MODE> && st == kBodyRetry) {
       // a wave threshold <= +0: the steps again, in signed order, on the row read again
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
