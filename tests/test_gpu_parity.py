@@ -365,6 +365,26 @@ def test_short_fp32_rows_with_top_k(v, k, p, t):
     _run_custom(wl)
 
 
+@pytest.mark.parametrize("name,rows,vocab", [("tiny_joint", None, None), ("joint_128k", 6, 16384),
+                                             ("topp_152k", 4, 8192), ("none_32k", 4, 8192)])
+def test_full_log_probs_into_an_unaligned_output(name, rows, vocab):
+    """Full-row log-probs into an output 4 bytes past a 16-byte boundary: the
+    kernels that store 16 bytes at a time are not chosen, the rows match the
+    oracle all the same."""
+    wl = synth.make(name, rows=rows, vocab=vocab)
+    print(f"[case] unaligned log_probs {name} rows={wl.n} vocab={wl.vocab}", flush=True)
+    dev = parity.to_device(wl)
+    s = tsa.Sampler(wl.vocab, wl.n)
+    buf = torch.empty(wl.n * wl.vocab + 4, dtype=torch.float32, device="cuda")
+    out = buf[1:1 + wl.n * wl.vocab].view(wl.n, wl.vocab)
+    assert out.data_ptr() % 16 == 4
+    s.log_probs(dev["logits"], dev["params"], n=wl.n, no_top_k=wl.no_top_k, no_top_p=wl.no_top_p,
+                gather_indices=dev["gather"], token_to_request_index=dev["req"], output=out)
+    torch.cuda.synchronize()
+    parity.compare_log_probs(out.cpu().numpy(), parity.oracle_log_probs(wl),
+                             parity.oracle_sample(wl)).check()
+
+
 def test_determinism_and_step_offset():
     wl = synth.make("spec_mix", rows=24, vocab=16384)
     dev = parity.to_device(wl)

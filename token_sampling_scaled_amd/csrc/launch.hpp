@@ -116,10 +116,10 @@ hipError_t launch_rows_topp(const RowArgs& a, DType dtype, hipStream_t stream);
 // full rows a write pass.
 hipError_t launch_rows_topp_lp(const RowArgs& a, DType dtype, OutMode mode, hipStream_t stream);
 
-// Short fp32 rows (up to 8192 entries) with top-k (sampling, top-k and joint
-// routes): register-resident kernel, one workgroup per row.
+// Short fp32 rows (up to 8192 entries) on the top-k and joint routes (sampling
+// and log-probs): register-resident kernel, one workgroup per row.
 bool small_f32_supported(const RowArgs& a, DType dtype, Route route, OutMode mode);
-hipError_t launch_rows_small_f32(const RowArgs& a, Route route, hipStream_t stream);
+hipError_t launch_rows_small_f32(const RowArgs& a, Route route, OutMode mode, hipStream_t stream);
 
 // The general multi-pass kernel alone (every row shape).
 hipError_t launch_rows_general(const RowArgs& a, DType dtype, Route route, OutMode mode,

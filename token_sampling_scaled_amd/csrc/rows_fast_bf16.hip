@@ -1446,7 +1446,10 @@ hipError_t launch_rows(const RowArgs& a, DType dtype, Route route, OutMode mode,
     return launch_rows_topp(a, dtype, stream);
   const bool aligned = (reinterpret_cast<uintptr_t>(a.logits) % 16) == 0 && (a.row_stride % 8) == 0;
   const int64_t nvec = a.vocab / 8;
-  const bool fast_shape = dtype == kBF16 && aligned && (a.vocab % 8) == 0 && nvec <= 16 * (int64_t)kB;
+  // full log-prob rows go out as 16-byte stores
+  const bool out_vec = mode != kOutLogProbFull || (reinterpret_cast<uintptr_t>(a.out_lp) % 16) == 0;
+  const bool fast_shape = dtype == kBF16 && aligned && (a.vocab % 8) == 0 && nvec <= 16 * (int64_t)kB &&
+                          out_vec;
   // log-probs of rows without top-k in any other shape (fp32 above all): the
   // top-p route's cutoff, then a write pass
   if (mode != kOutSample && (route == kRouteTopP || route == kRouteNone) && !fast_shape &&
@@ -1464,7 +1467,7 @@ hipError_t launch_rows(const RowArgs& a, DType dtype, Route route, OutMode mode,
     return launch_nv<16>(a, route, mode, stream);
   }
   // short fp32 rows with top-k: their own register-resident kernel
-  if (small_f32_supported(a, dtype, route, mode)) return launch_rows_small_f32(a, route, stream);
+  if (small_f32_supported(a, dtype, route, mode)) return launch_rows_small_f32(a, route, mode, stream);
   return launch_rows_general(a, dtype, route, mode, stream);
 }
 

@@ -49,6 +49,8 @@ struct SmallShared {
   float sz[kMaxK];                  // ... and perturbed scores x/T + g
   uint32_t wtot[kWv];
   uint32_t wmax[kWv];               // per-wave largest order key
+  uint64_t lastw;                   // log-probs: rank word of P's last member ...
+  float lzp;                        // ... and ln Z_P
   uint32_t nc;                      // candidates appended so far
   uint32_t bstar;                   // lowest candidate bin
   uint32_t ncand;                   // entries in the bins at and above it
@@ -63,7 +65,81 @@ __device__ __forceinline__ float value_of_key(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-template <int ROUTE>
+// Step 4 (wave 0; lane l holds entries 4l .. 4l+3 of K): P inside K, then the
+// draw (sampling), or the last member of P and ln Z_P for every thread
+// (log-probs).
+template <int ROUTE, int MODE>
+__device__ __forceinline__ void draw_or_cut(const RowArgs& a, int r, SmallShared& sm, uint32_t kk,
+                                            float pq, float inv_t, float m) {
+  constexpr bool kHasP = ROUTE == kRouteJoint;
+  const int lane = threadIdx.x & (kWave - 1);
+  float x[4], w[4], zz[4], pre[4];
+  int32_t jj[4];
+  float lsum = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t i = 4u * lane + e;
+    const uint64_t rw = i < kk ? sm.sorted[i] : 0ull;
+    jj[e] = (int32_t)~(uint32_t)rw;
+    x[e] = i < kk ? value_of_key((uint32_t)(rw >> 32)) : 0.0f;
+    w[e] = i < kk ? sm.sw[i] : 0.0f;
+    zz[e] = (MODE == kOutSample && i < kk) ? sm.sz[i] : -__builtin_inff();
+    pre[e] = lsum;                   // mass of the entries before it, inside the lane
+    lsum += w[e];
+  }
+  const float li = wave_scan_f32(lsum);
+  const float zk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(li), kWave - 1));
+  const float lex = li - lsum;
+  // the first tie group (after the top one) whose mass before it reaches
+  // p * Z_K starts the entries left out
+  uint32_t cut = kk;
+  if (kHasP && pq < 1.0f - 1e-6f) {
+    const float xprev = __shfl_up(x[3], 1, kWave);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t i = 4u * lane + e;
+      const float xp = e == 0 ? xprev : x[e - 1];
+      const bool start = i > 0 && i < kk && x[e] != xp;
+      if (start && (lex + pre[e]) / zk >= pq && i < cut) cut = i;
+    }
+    cut = wave_min_dpp(cut);
+  }
+  float zl = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) zl += (4u * lane + e < cut) ? w[e] : 0.0f;
+  const float zp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_scan_f32(zl)), kWave - 1));
+  if constexpr (MODE != kOutSample) {
+    if (lane == 0) {
+      sm.lastw = sm.sorted[cut - 1];
+      sm.lzp = __logf(zp);
+    }
+    return;
+  }
+
+  ArgBest best{-__builtin_inff(), 0x7FFFFFFF};
+  float sbest = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t i = 4u * lane + e;
+    if (i < cut && better(zz[e], jj[e], best.z, best.j)) {
+      best = ArgBest{zz[e], jj[e]};
+      sbest = __fmul_rn(x[e], inv_t);
+    }
+  }
+  // the largest score, the smallest index among equal ones
+  const float zmax = wave_max_f32_dpp(best.z);
+  const bool top = best.z == zmax;
+  const uint32_t jmin = wave_min_dpp(top ? (uint32_t)best.j : 0xFFFFFFFFu);
+  const unsigned long long own = __ballot(top && (uint32_t)best.j == jmin);
+  const int sl = __ffsll((long long)own) - 1;
+  const float sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sbest), sl));
+  if (lane == 0) {
+    a.out_ids[r] = (int32_t)jmin;
+    if (a.out_lp) a.out_lp[r] = sw - m - __logf(zp);
+  }
+}
+
+template <int ROUTE, int MODE>
 __global__ __launch_bounds__(kB) void rows_small_f32_kernel(RowArgs a) {
   constexpr bool kHasP = ROUTE == kRouteJoint;
   __shared__ Shared sh;
@@ -88,7 +164,7 @@ __global__ __launch_bounds__(kB) void rows_small_f32_kernel(RowArgs a) {
   const float pq = kHasP ? a.top_p[q] : 1.0f;
   const uint64_t seed = a.seed[q];
   if (!(temp >= 1e-5f) || !(kq >= 1 && (int64_t)kq < a.vocab) || kq > kMaxK) {
-    general::general_row<float, ROUTE, kOutSample>(a, r, sh.g);
+    general::general_row<float, ROUTE, MODE>(a, r, sh.g);
     return;
   }
 
@@ -130,7 +206,7 @@ __global__ __launch_bounds__(kB) void rows_small_f32_kernel(RowArgs a) {
   }
   if (total == 0 || kmx >= kPosInfKey) {   // no finite entry, or a +inf
     __syncthreads();
-    general::general_row<float, ROUTE, kOutSample>(a, r, sh.g);
+    general::general_row<float, ROUTE, MODE>(a, r, sh.g);
     return;
   }
   const uint32_t kk = min((uint32_t)kq, total);   // |K|
@@ -145,7 +221,7 @@ __global__ __launch_bounds__(kB) void rows_small_f32_kernel(RowArgs a) {
   const uint32_t ncand = sm.ncand;
   if (ncand > (uint32_t)kCandCap) {
     __syncthreads();
-    general::general_row<float, ROUTE, kOutSample>(a, r, sh.g);
+    general::general_row<float, ROUTE, MODE>(a, r, sh.g);
     return;
   }
 
@@ -196,87 +272,80 @@ __global__ __launch_bounds__(kB) void rows_small_f32_kernel(RowArgs a) {
       const float sv = __fmul_rn(value_of_key((uint32_t)(mine >> 32)), inv_t);
       sm.sorted[rank] = mine;
       sm.sw[rank] = expf(sv - m);
-      sm.sz[rank] = sv + gumbel_from_word(nst.word(~(uint32_t)mine));
+      if constexpr (MODE == kOutSample) sm.sz[rank] = sv + gumbel_from_word(nst.word(~(uint32_t)mine));
     }
   }
   __syncthreads();
-  if (wid != 0) return;
+  if (wid == 0) draw_or_cut<ROUTE, MODE>(a, r, sm, kk, pq, inv_t, m);
+  if constexpr (MODE == kOutSample) return;
+  __syncthreads();
 
-  // ---- 4. P inside K and the draw (wave 0; lane l holds entries 4l .. 4l+3 of K)
-  float x[4], w[4], zz[4], pre[4];
-  int32_t jj[4];
-  float lsum = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t i = 4u * lane + e;
-    const uint64_t rw = i < kk ? sm.sorted[i] : 0ull;
-    jj[e] = (int32_t)~(uint32_t)rw;
-    x[e] = i < kk ? value_of_key((uint32_t)(rw >> 32)) : 0.0f;
-    w[e] = i < kk ? sm.sw[i] : 0.0f;
-    zz[e] = i < kk ? sm.sz[i] : -__builtin_inff();
-    pre[e] = lsum;                   // mass of the entries before it, inside the lane
-    lsum += w[e];
-  }
-  const float li = wave_scan_f32(lsum);
-  const float zk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(li), kWave - 1));
-  const float lex = li - lsum;
-  // the first tie group (after the top one) whose mass before it reaches
-  // p * Z_K starts the entries left out
-  uint32_t cut = kk;
-  if (kHasP && pq < 1.0f - 1e-6f) {
-    const float xprev = __shfl_up(x[3], 1, kWave);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t i = 4u * lane + e;
-      const float xp = e == 0 ? xprev : x[e - 1];
-      const bool start = i > 0 && i < kk && x[e] != xp;
-      if (start && (lex + pre[e]) / zk >= pq && i < cut) cut = i;
+  // ---- 5. log-probs: lp = x/T - m - ln Z_P on P (the first `cut` members of
+  // K in the order: rank word at or above the last one's), -inf elsewhere
+  const uint64_t lastw = sm.lastw;
+  const float lzp = sm.lzp;
+  if constexpr (MODE == kOutLogProbAt) {
+    if (tid == 0) {
+      const int64_t j = a.token_ids[r];
+      float out = -__builtin_inff();
+      if (j >= 0 && j < a.vocab) {
+        const float x = static_cast<const float*>(a.logits)[src * a.row_stride + j];
+        const uint32_t k = KeyF32::from_bits(__float_as_uint(x));
+        if (k > KeyF32::kNegInf && rank_word(k, (int32_t)j) >= lastw) out = __fmul_rn(x, inv_t) - m - lzp;
+      }
+      a.out_lp[r] = out;
     }
-    cut = wave_min_dpp(cut);
-  }
-  float zl = 0.0f;
+  } else {
+    f32x4* out_row = reinterpret_cast<f32x4*>(a.out_lp + (int64_t)r * a.vocab);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) zl += (4u * lane + e < cut) ? w[e] : 0.0f;
-  const float zp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_scan_f32(zl)), kWave - 1));
-
-  ArgBest best{-__builtin_inff(), 0x7FFFFFFF};
-  float sbest = 0.0f;
+    for (int i = 0; i < kNV; ++i) {
+      const int vi = i * kB + tid;
+      if (vi >= nvec) continue;
+      float o[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t i = 4u * lane + e;
-    if (i < cut && better(zz[e], jj[e], best.z, best.j)) {
-      best = ArgBest{zz[e], jj[e]};
-      sbest = __fmul_rn(x[e], inv_t);
+      for (int e = 0; e < 4; ++e) {
+        const bool in_p = key[i][e] > KeyF32::kNegInf && rank_word(key[i][e], vi * 4 + e) >= lastw;
+        o[e] = in_p ? __fmul_rn(d[i][e], inv_t) - m - lzp : -__builtin_inff();
+      }
+      out_row[vi] = f32x4{o[0], o[1], o[2], o[3]};
     }
-  }
-  // the largest score, the smallest index among equal ones
-  const float zmax = wave_max_f32_dpp(best.z);
-  const bool top = best.z == zmax;
-  const uint32_t jmin = wave_min_dpp(top ? (uint32_t)best.j : 0xFFFFFFFFu);
-  const unsigned long long own = __ballot(top && (uint32_t)best.j == jmin);
-  const int sl = __ffsll((long long)own) - 1;
-  const float sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sbest), sl));
-  if (lane == 0) {
-    a.out_ids[r] = (int32_t)jmin;
-    if (a.out_lp) a.out_lp[r] = sw - m - __logf(zp);
   }
 }
 
 }  // namespace
 
 bool small_f32_supported(const RowArgs& a, DType dtype, Route route, OutMode mode) {
-  return dtype == kF32 && mode == kOutSample && (route == kRouteTopK || route == kRouteJoint) &&
+  // full log-prob rows go out as 16-byte stores
+  const bool out_vec = mode != kOutLogProbFull || (reinterpret_cast<uintptr_t>(a.out_lp) % 16) == 0;
+  return dtype == kF32 && (route == kRouteTopK || route == kRouteJoint) && out_vec &&
          a.vocab >= 4 && a.vocab <= (int64_t)kNV * 4 * kB && (a.vocab % 4) == 0 &&
          (a.row_stride % 4) == 0 && (reinterpret_cast<uintptr_t>(a.logits) % 16) == 0;
 }
 
-hipError_t launch_rows_small_f32(const RowArgs& a, Route route, hipStream_t stream) {
-  if (a.n <= 0) return hipSuccess;
+namespace {
+template <int ROUTE>
+void launch_mode(const RowArgs& a, OutMode mode, hipStream_t stream) {
   const dim3 grid(a.n), block(kB);
+  switch (mode) {
+    case kOutSample:
+      hipLaunchKernelGGL((rows_small_f32_kernel<ROUTE, kOutSample>), grid, block, 0, stream, a);
+      break;
+    case kOutLogProbFull:
+      hipLaunchKernelGGL((rows_small_f32_kernel<ROUTE, kOutLogProbFull>), grid, block, 0, stream, a);
+      break;
+    default:
+      hipLaunchKernelGGL((rows_small_f32_kernel<ROUTE, kOutLogProbAt>), grid, block, 0, stream, a);
+      break;
+  }
+}
+}  // namespace
+
+hipError_t launch_rows_small_f32(const RowArgs& a, Route route, OutMode mode, hipStream_t stream) {
+  if (a.n <= 0) return hipSuccess;
   if (route == kRouteJoint)
-    hipLaunchKernelGGL(rows_small_f32_kernel<kRouteJoint>, grid, block, 0, stream, a);
+    launch_mode<kRouteJoint>(a, mode, stream);
   else
-    hipLaunchKernelGGL(rows_small_f32_kernel<kRouteTopK>, grid, block, 0, stream, a);
+    launch_mode<kRouteTopK>(a, mode, stream);
   return hipGetLastError();
 }
 

@@ -1185,14 +1185,16 @@ hipError_t launch_rows_topp_lp(const RowArgs& a, DType dtype, OutMode mode, hipS
   const int32_t ntiles = (int32_t)((groups + kDrawTile - 1) / kDrawTile);
   const uintptr_t base = reinterpret_cast<uintptr_t>(a.logits);
   const bool full = mode == kOutLogProbFull;
+  // the write pass stores four log-probs at a time (16 bytes)
+  const bool out_vec = !full || (reinterpret_cast<uintptr_t>(a.out_lp) % 16) == 0;
   if (dtype == kF32) {
-    const bool vec = (base % 16) == 0 && (a.row_stride % 4) == 0 && (a.vocab % 4) == 0;
+    const bool vec = (base % 16) == 0 && (a.row_stride % 4) == 0 && (a.vocab % 4) == 0 && out_vec;
     if (vec) return full ? launch_lp_typed<float, true, kOutLogProbFull>(a, ntiles, stream)
                          : launch_lp_typed<float, true, kOutLogProbAt>(a, ntiles, stream);
     return full ? launch_lp_typed<float, false, kOutLogProbFull>(a, ntiles, stream)
                 : launch_lp_typed<float, false, kOutLogProbAt>(a, ntiles, stream);
   }
-  const bool vec = (base % 8) == 0 && (a.row_stride % 4) == 0 && (a.vocab % 4) == 0;
+  const bool vec = (base % 8) == 0 && (a.row_stride % 4) == 0 && (a.vocab % 4) == 0 && out_vec;
   if (vec) return full ? launch_lp_typed<uint16_t, true, kOutLogProbFull>(a, ntiles, stream)
                        : launch_lp_typed<uint16_t, true, kOutLogProbAt>(a, ntiles, stream);
   return full ? launch_lp_typed<uint16_t, false, kOutLogProbFull>(a, ntiles, stream)
