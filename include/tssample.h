@@ -149,7 +149,9 @@ ts_status ts_sample(ts_sampler* sampler, const void* logits, ts_dtype dtype,
  * with no finite logit: NaN).  Arguments as for ts_sample, plus
  *   token_ids  device int32 [n] or NULL
  *   out        device float: [n, vocab] row-major when token_ids is NULL, else [n]
- *              holding lp at token_ids[r]
+ *              holding lp at token_ids[r].  Any float alignment is accepted; full
+ *              rows into a 16-byte aligned buffer take the kernels that store 16
+ *              bytes at a time
  * Errors: as ts_sample. */
 ts_status ts_log_probs(ts_sampler* sampler, const void* logits, ts_dtype dtype,
                        int64_t rows_in_buffer, int64_t row_stride, int32_t n,
