@@ -11,8 +11,8 @@
 //      then issues each load of the second half as a first-half vector
 //      arrives (a wave blocked on a load issue could not work on data it
 //      already holds), and takes t_w = the c-th largest of its 16-entry group
-//      maxima over the first half (bitwise descent with ballots),
-//      c = min(k, ceil(k/16) + 4);
+//      maxima over its first quarter (bitwise descent with ballots),
+//      c = min(k, ceil(k/32) + 4);
 //   2. filter: a 16-byte vector whose maximum reaches t_w is copied whole into
 //      the wave's LDS segment (ballot + mbcnt), and its entries >= t_w are
 //      counted in a histogram with one bin per bf16 value (a bin is exactly one
@@ -30,10 +30,14 @@
 //      member per thread -- and the perturbed argmax picks the id.
 // Comparisons use the bf16 bit patterns as signed 16-bit integers: for positive
 // values that is the value order and every negative value sorts below them, so
-// it is exact whenever every t_w > +0.  Greedy rows take the first maximum.
-// Every other row -- no top-k, k > 1024, some t_w <= +0, NaN logits, a full
-// LDS segment, or fewer than k counted entries at or above t* -- runs the
-// general per-row body (general_row.hpp) on the same workgroup.
+// it is exact whenever every t_w > +0.  A row with some t_w <= +0 runs steps
+// 1-5 again on the row read again and taken to two's-complement order, with
+// the patterns of |x| < 2^-64 sharing one histogram key (see sord2 and zkey).
+// Rows without top-k run nok_row (the whole row in registers).  Greedy rows
+// take the first maximum.  Every other row -- k > 1024, NaN logits, a full LDS
+// segment, fewer than k counted entries at or above t*, a cut inside the
+// collapsed zone -- runs the general per-row body (general_row.hpp) on the
+// same workgroup.
 #include "general_row.hpp"
 
 namespace tss {

@@ -12,7 +12,10 @@
 //     the others, and the first |K| land sorted.
 //  4. One wave: masses exp(x/T - m) of K in that order, the tie groups from the
 //     top whose mass before them stays below p * Z_K (at least one), then
-//     Philox noise for each member of P and the argmax of x/T + g.
+//     Philox noise for each member of P and the argmax of x/T + g; or, for
+//     log-probs, the rank word of P's last member and ln Z_P, after which
+//     every thread writes its own entries (full rows) or thread 0 the one at
+//     the request's id.
 //
 // The ranking threads also weigh their members of K and draw their noise, so
 // that wave 0 is left with two prefix sums and an argmax.  Rows the body does
