@@ -304,8 +304,9 @@ def test_bf16_like_ties_and_misaligned_stride(dtype):
 
 def _signed_bf16_rows(v, seed):
     """bf16 rows whose top-k cut is at or below zero: all negative, crossing
-    zero, signed zeros at the cut, and values inside |x| < 2^-64 (the zone the
-    register-resident kernel's second pass cannot cut in: general body)."""
+    zero, signed zeros at the cut, values inside |x| < 2^-64 (the zone the
+    register-resident kernel's second pass cannot cut in: general body), and
+    negatives mixed with -inf and NaN of both signs."""
     rng = np.random.default_rng(seed)
     rows = np.empty((6, v), dtype=np.float32)
     rows[0] = rng.normal(-20.0, 3.0, v)
@@ -316,6 +317,9 @@ def _signed_bf16_rows(v, seed):
     rows[4] = rng.normal(-3.0, 2.0, v)
     rows[4, rng.choice(v, 5, replace=False)] = 6.0
     rows[5] = -rng.exponential(1.0, v)
+    rows[5, rng.choice(v, v // 16, replace=False)] = -np.inf
+    rows[5, rng.choice(v, 7, replace=False)] = np.nan
+    rows[5, rng.choice(v, 7, replace=False)] = -np.nan
     return rows
 
 
