@@ -46,9 +46,12 @@
  *     has reached them.  A sampler handle may be used from one host thread at
  *     a time.
  *   - Errors are returned as ts_status, never thrown.  Host-checkable argument
- *     errors are detected before any work is enqueued.  Out-of-range values
- *     inside device arrays (gather / map / token ids) are the caller's
- *     responsibility and are not checked.
+ *     errors are detected before any work is enqueued.  Gather and request
+ *     indices inside device arrays are read without a guard (an out-of-range
+ *     one is undefined behaviour); a caller that does not trust them checks
+ *     them first with ts_check_indices, which writes a device error word.
+ *     Token ids are guarded: one outside [0, vocab) has a defined result
+ *     (ts_log_probs, ts_raw_log_probs_at).
  */
 #ifndef TSSAMPLE_H
 #define TSSAMPLE_H
@@ -149,7 +152,8 @@ ts_status ts_sample(ts_sampler* sampler, const void* logits, ts_dtype dtype,
  * with no finite logit: NaN).  Arguments as for ts_sample, plus
  *   token_ids  device int32 [n] or NULL
  *   out        device float: [n, vocab] row-major when token_ids is NULL, else [n]
- *              holding lp at token_ids[r].  Any float alignment is accepted; full
+ *              holding lp at token_ids[r] (-inf for an id outside [0, vocab)).
+ *              Any float alignment is accepted; full
  *              rows into a 16-byte aligned buffer take the kernels that store 16
  *              bytes at a time
  * Errors: as ts_sample. */
@@ -190,6 +194,25 @@ ts_status ts_raw_log_probs_at(ts_sampler* sampler, const void* logits, ts_dtype 
 ts_status ts_build_spec_map(int32_t num_decode, int32_t num_prefill, int32_t num_spec,
                             int32_t* out_map, int32_t capacity, int32_t on_device,
                             void* stream, int32_t* out_n);
+
+/* Debug check of the device index arrays of a ts_sample / ts_log_probs call,
+ * whose values those calls read through without a guard (see the conventions
+ * at the top of this file).  For callers that do not trust them; not part of
+ * the pages' operation.
+ *   n, gather_indices, rows_in_buffer, token_to_request_index  as for ts_sample
+ *                   (either array may be NULL: it is then not checked)
+ *   num_requests    the parameter slots (params->num_requests)
+ *   error_word      device uint32 [1], written: 0, or TS_INDEX_GATHER_OUT (a
+ *                   gather index outside [0, rows_in_buffer)) | TS_INDEX_REQUEST_OUT
+ *                   (a request index outside [0, num_requests))
+ * Enqueued on `stream` (hipStream_t); no handle, no workspace.
+ * Errors: TS_E_ARG (n < 0, error_word NULL, rows_in_buffer < 1 with a gather
+ * array, num_requests < 1 with a request array), TS_E_HIP. */
+#define TS_INDEX_GATHER_OUT 1u
+#define TS_INDEX_REQUEST_OUT 2u
+ts_status ts_check_indices(int32_t n, const int32_t* gather_indices, int64_t rows_in_buffer,
+                           const int32_t* token_to_request_index, int32_t num_requests,
+                           uint32_t* error_word, void* stream);
 
 /* Chain verification of speculative drafts against the target's samples (the
  * verify step of the TokenSpeed Triton sampling backend page,

@@ -158,6 +158,15 @@ def test_raw_log_probs_argument_checks_on_validation_handle(lib):
         lib.ts_destroy(h)
 
 
+def test_check_indices_argument_checks(lib):
+    # every argument error returns before any GPU call
+    assert lib.ts_check_indices(-1, FAKE, 8, None, 0, FAKE, None) == tsa.TS_E_ARG
+    assert lib.ts_check_indices(4, FAKE, 8, None, 0, None, None) == tsa.TS_E_ARG
+    assert lib.ts_check_indices(4, FAKE, 0, None, 0, FAKE, None) == tsa.TS_E_ARG
+    assert lib.ts_check_indices(4, None, 0, FAKE, 0, FAKE, None) == tsa.TS_E_ARG
+    assert lib.ts_check_indices(4, FAKE, -3, FAKE, 2, FAKE, None) == tsa.TS_E_ARG
+
+
 def test_verify_chain_argument_checks(lib):
     # error paths and the empty batch return before any GPU call
     assert lib.ts_verify_chain(0, 4, None, None, None, None, None, None) == tsa.TS_OK

@@ -645,3 +645,34 @@ def test_verify_chain_on_sampled_speculative_rows():
     e = tsa.verify_chain(torch.empty((0, 4), dtype=torch.int32, device="cuda"),
                          torch.empty(0, dtype=torch.int32, device="cuda"))
     assert e[0].numel() == 0 and e[2].numel() == 0
+
+
+@pytest.mark.parametrize("n", [1, 63, 1000, 300001])
+def test_check_indices_flags_out_of_range_entries(n):
+    """The debug index check against the definition: the gather bit is set iff
+    some gather index falls outside [0, rows), the request bit iff some request
+    index falls outside [0, Q); arrays left out are not checked."""
+    rng = np.random.default_rng(n)
+    rows, q = 2 * n + 3, max(1, n // 3)
+    print(f"[case] check_indices n={n}", flush=True)
+    for trial in range(6):
+        g = rng.integers(0, rows, n).astype(np.int32)
+        m = rng.integers(0, q, n).astype(np.int32)
+        if trial in (1, 3):
+            g[rng.integers(0, n)] = rows if trial == 1 else -1
+        if trial in (2, 3):
+            m[rng.integers(0, n)] = q if trial == 2 else -7
+        if trial == 4:
+            g[-1] = np.iinfo(np.int32).max
+            m[0] = np.iinfo(np.int32).min
+        want = (tsa.INDEX_GATHER_OUT if ((g < 0) | (g >= rows)).any() else 0) | \
+               (tsa.INDEX_REQUEST_OUT if ((m < 0) | (m >= q)).any() else 0)
+        gd, md = torch.from_numpy(g).cuda(), torch.from_numpy(m).cuda()
+        got = tsa.check_indices(n, gather_indices=gd, rows_in_buffer=rows,
+                                token_to_request_index=md, num_requests=q)
+        assert int(got.item()) == want, (trial, int(got.item()), want)
+        only_g = tsa.check_indices(n, gather_indices=gd, rows_in_buffer=rows)
+        only_m = tsa.check_indices(n, token_to_request_index=md.long(), num_requests=q)
+        assert int(only_g.item()) == want & tsa.INDEX_GATHER_OUT
+        assert int(only_m.item()) == want & tsa.INDEX_REQUEST_OUT
+    assert int(tsa.check_indices(0, device="cuda").item()) == 0

@@ -69,11 +69,13 @@ def library() -> ctypes.CDLL:
                                       ctypes.POINTER(c_i32)]
     lib.ts_verify_chain.argtypes = [c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
     lib.ts_apply_vocab_mask.argtypes = [c_i64, c_vp, c_i32, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp]
+    lib.ts_check_indices.argtypes = [c_i32, c_vp, c_i64, c_vp, c_i32, c_vp, c_vp]
     lib.ts_select_route.argtypes = [c_i32, c_i32]
     lib.ts_status_str.argtypes = [c_i32]
     lib.ts_status_str.restype = ctypes.c_char_p
     for name in ("ts_create", "ts_destroy", "ts_sample", "ts_log_probs", "ts_raw_log_probs_at",
-                 "ts_build_spec_map", "ts_verify_chain", "ts_apply_vocab_mask", "ts_select_route"):
+                 "ts_build_spec_map", "ts_verify_chain", "ts_apply_vocab_mask", "ts_select_route",
+                 "ts_check_indices"):
         getattr(lib, name).restype = ctypes.c_int32
     _lib = lib
     return lib
@@ -358,5 +360,30 @@ def apply_vocab_mask(logits: torch.Tensor, mask: torch.Tensor,
     return logits
 
 
+INDEX_GATHER_OUT, INDEX_REQUEST_OUT = 1, 2
+
+
+def check_indices(n: int, *, gather_indices: Optional[torch.Tensor] = None,
+                  rows_in_buffer: int = 0,
+                  token_to_request_index: Optional[torch.Tensor] = None,
+                  num_requests: int = 0, device=None) -> torch.Tensor:
+    """Debug check of the index arrays a sampling call would read through
+    unguarded: a device int32 [1] holding 0, or INDEX_GATHER_OUT (a gather index
+    outside [0, rows_in_buffer)) | INDEX_REQUEST_OUT (a request index outside
+    [0, num_requests)), enqueued on the current stream (ts_check_indices)."""
+    src = gather_indices if gather_indices is not None else token_to_request_index
+    dev = torch.device(device) if device is not None else (src.device if src is not None else None)
+    if dev is None or dev.type != "cuda":
+        raise ValueError("check_indices needs a GPU device (or an index tensor on one)")
+    g = _index_i32(gather_indices, "gather_indices", n, dev)
+    q = _index_i32(token_to_request_index, "token_to_request_index", n, dev)
+    word = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(library().ts_check_indices(int(n), _ptr(g), int(rows_in_buffer), _ptr(q),
+                                      int(num_requests), _ptr(word), _stream(dev)),
+           "ts_check_indices")
+    return word
+
+
 __all__ = ["Sampler", "SamplingParams", "build_spec_map", "verify_chain", "select_route",
-           "apply_vocab_mask", "library", "LIB_PATH"]
+           "apply_vocab_mask", "check_indices", "INDEX_GATHER_OUT", "INDEX_REQUEST_OUT",
+           "library", "LIB_PATH"]

@@ -129,6 +129,14 @@ hipError_t launch_rows_general(const RowArgs& a, DType dtype, Route route, OutMo
 hipError_t launch_spec_map(int32_t num_decode, int32_t num_prefill, int32_t num_spec,
                            int32_t* out_map, hipStream_t stream);
 
+// Debug check of a call's device index arrays: clears *word, then ORs in
+// kIndexGatherOut for a gather index outside [0, rows) and kIndexRequestOut
+// for a request index outside [0, num_requests).
+constexpr uint32_t kIndexGatherOut = 1u;
+constexpr uint32_t kIndexRequestOut = 2u;
+hipError_t launch_check_indices(int32_t n, const int32_t* gather, int64_t rows, const int32_t* req,
+                                int32_t num_requests, uint32_t* word, hipStream_t stream);
+
 // Chain verification of speculative drafts (one thread per request).
 hipError_t launch_verify_chain(int32_t bs, int32_t n, const int32_t* candidates,
                                const int32_t* target_sampled, int32_t* predicts,

@@ -315,4 +315,16 @@ ts_status ts_verify_chain(int32_t bs, int32_t n_per_req, const int32_t* candidat
              : TS_E_HIP;
 }
 
+ts_status ts_check_indices(int32_t n, const int32_t* gather_indices, int64_t rows_in_buffer,
+                           const int32_t* token_to_request_index, int32_t num_requests,
+                           uint32_t* error_word, void* stream) {
+  if (n < 0 || error_word == nullptr) return TS_E_ARG;
+  if (gather_indices != nullptr && rows_in_buffer < 1) return TS_E_ARG;
+  if (token_to_request_index != nullptr && num_requests < 1) return TS_E_ARG;
+  return tss::launch_check_indices(n, gather_indices, rows_in_buffer, token_to_request_index,
+                                   num_requests, error_word, (hipStream_t)stream) == hipSuccess
+             ? TS_OK
+             : TS_E_HIP;
+}
+
 }  // extern "C"
