@@ -85,6 +85,11 @@ struct FastShared {
   uint32_t tmax;                   // largest wave threshold published so far
   uint32_t kmax;                   // row maximum (unsigned image of the signed order)
   float mrow;                      // row maximum / T (scan result)
+  uint32_t occ[4];                 // signed-order pass: bit b set when a counted key
+                                   // lies in [256 b, 256 b + 255]
+  uint32_t bcnt[128];              // signed-order pass, per occupied block of the window
+  float bmass[128];                // (ordinal from the top): count and mass of its
+                                   // entries in the window
 };
 
 // Rows without an active top-k: an exact histogram of order keys over the
@@ -356,39 +361,139 @@ __device__ __forceinline__ float bin_weight(int32_t b, float inv_t, float m, int
   return __expf(__fmaf_rn(bits_value(so ? sord_value16(zkey_pat(b - hoff)) : b), inv_t, -m));
 }
 
-// Whether any of the bins [lo, top] of the chunk of 256 bins below top holds
-// an entry (wave-uniform).
-__device__ __forceinline__ bool chunk_any(const uint32_t* hist, int32_t top, int32_t lo, int lane) {
-  uint32_t c = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int32_t b = top - (4 * lane + i);
-    c |= b >= lo ? hist_get(hist, b > 0 ? b : 0) : 0u;
+// Whether any of the bins [max(top - 255, lo), top] may hold an entry, from
+// the occupancy bits of the 256-key blocks (occ_lo: blocks 0..63, occ_hi:
+// 64..127; wave-uniform).  The chunk meets at most two blocks.
+__device__ __forceinline__ bool chunk_occupied(uint64_t occ_lo, uint64_t occ_hi, int32_t top,
+                                               int32_t lo) {
+  const int32_t bh = top >> 8;
+  const int32_t bl = (top - 255 > lo ? top - 255 : lo) >> 8;
+  const uint64_t mh = bh < 64 ? occ_lo >> bh : occ_hi >> (bh - 64);
+  const uint64_t ml = bl < 64 ? occ_lo >> bl : occ_hi >> (bl - 64);
+  return ((mh | ml) & 1u) != 0;
+}
+
+// The highest occupied block below block i (i <= 128), or -1.
+__device__ __forceinline__ int32_t occupied_below(uint64_t occ_lo, uint64_t occ_hi, int32_t i) {
+  if (i > 64) {
+    const uint64_t mh = i >= 128 ? occ_hi : occ_hi & ((1ull << (i - 64)) - 1ull);
+    if (mh) return 127 - (int32_t)__clzll((long long)mh);
   }
-  return __ballot(c != 0) != 0;
+  const uint64_t ml = i >= 64 ? occ_lo : occ_lo & ((1ull << i) - 1ull);
+  return ml ? 63 - (int32_t)__clzll((long long)ml) : -1;
+}
+
+// Next chunk top after an empty chunk ending at top (bins >= lo): the top of
+// the highest occupied block below it, plus 256 for the loop's step; below
+// lo when no occupied block remains.
+__device__ __forceinline__ int32_t skip_empty(uint64_t occ_lo, uint64_t occ_hi, int32_t top,
+                                              int32_t lo) {
+  const int32_t nb = occupied_below(occ_lo, occ_hi, (top - 255 > lo ? top - 255 : lo) >> 8);
+  return nb < 0 ? lo - 1 + 4 * kWave : nb * 256 + 255 + 4 * kWave;
+}
+
+// Counts and masses of the occupied 256-key blocks of the window [lo, hi]
+// (hi the top bin of a block), the block of ordinal o (from the top) taken by
+// wave o mod 16, as the scan below adds them up; every wave returns the
+// number of such blocks.  The one-wave scan then starts at the blocks where k
+// and the top-p mass are reached instead of walking every block above them.
+__device__ __forceinline__ int32_t block_totals(const uint32_t* hist, const uint32_t* occ,
+                                                uint32_t* bcnt, float* bmass, int32_t lo,
+                                                int32_t hi, float inv_t, float m, int32_t hoff,
+                                                int wid, int lane) {
+  const uint64_t occ_lo = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)occ[0]) |
+                          ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)occ[1]) << 32);
+  const uint64_t occ_hi = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)occ[2]) |
+                          ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)occ[3]) << 32);
+  int32_t ord = 0;
+  for (int32_t b = occupied_below(occ_lo, occ_hi, (hi >> 8) + 1); b >= (lo >> 8);
+       b = occupied_below(occ_lo, occ_hi, b), ++ord) {
+    if ((ord & (kWv - 1)) != wid) continue;
+    const int32_t top = b * 256 + 255;
+    uint32_t cs = 0;
+    float ms = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int32_t bin = top - (4 * lane + i);
+      const uint32_t c = bin >= lo ? hist_get(hist, bin) : 0u;
+      const float w = bin_weight(bin, inv_t, m, hoff, true);
+      cs += c;
+      ms += c ? (float)c * w : 0.0f;
+    }
+    const uint32_t ci = wave_scan_u32(cs);
+    const float mi = wave_scan_f32(ms);
+    if (lane == kWave - 1) {
+      bcnt[ord] = ci;
+      bmass[ord] = mi;
+    }
+  }
+  return ord;
 }
 
 // Scan the bins [lo, hi] (hi = the row maximum's) from the top; with so (wide
-// windows of signed-order keys, mostly empty), chunks without entries are
-// passed over.
+// windows of signed-order keys, mostly empty), the scan jumps from an empty
+// chunk to the highest occupied 256-key block (occ) below it.
 // Lane l takes bins top - 4l .. top - 4l - 3 of each 256-bin chunk.  When the
 // k-th value falls in the first chunk (the common case) the top-p cutoff is
 // found from the same registers; otherwise a second pass recomputes the masses.
 // The cutoff group is the first one, from the top, whose cumulative K-mass
 // reaches p * Z_K; the top group is always kept.
-__device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, int32_t hi,
-                                             float inv_t, float m, uint32_t k, bool p_on,
-                                             float p, int32_t hoff, bool so) {
+// With a block index (nblk >= 0: block_totals' counts and masses, hi a
+// block's top), the first pass starts at the block where the count reaches k
+// and the second at the block where the mass reaches p * Z_K.
+__device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, const uint32_t* occ,
+                                             int32_t lo, int32_t hi, float inv_t, float m,
+                                             uint32_t k, bool p_on, float p, int32_t hoff,
+                                             bool so, const uint32_t* bcnt = nullptr,
+                                             const float* bmass = nullptr, int32_t nblk = -1) {
   const int lane = threadIdx.x & (kWave - 1);
+  uint64_t occ_lo = 0, occ_hi = 0;
+  if (so) {
+    occ_lo = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)occ[0]) |
+             ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)occ[1]) << 32);
+    occ_hi = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)occ[2]) |
+             ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)occ[3]) << 32);
+  }
   ScanOut o{false, 0, 0, 0, 0, 0.0f};
   uint32_t cbase = 0, n_gt = 0;
   float mbase = 0.0f, mass_gt = 0.0f;
   bool in_first = true;
+  int32_t top1 = hi;
+  // block index: lane l holds blocks l and 64 + l (inclusive prefixes)
+  const bool bidx = so && nblk >= 0;
+  float f0 = 0.0f, f1 = 0.0f;
+  int32_t ok_blk = 0;
+  if (bidx) {
+    const uint32_t c0 = lane < nblk ? bcnt[lane] : 0u;
+    const uint32_t c1 = lane + kWave < nblk ? bcnt[lane + kWave] : 0u;
+    const float m0 = lane < nblk ? bmass[lane] : 0.0f;
+    const float m1 = lane + kWave < nblk ? bmass[lane + kWave] : 0.0f;
+    const uint32_t i0 = wave_scan_u32(c0);
+    const uint32_t i1 = wave_scan_u32(c1) + (uint32_t)__builtin_amdgcn_readlane((int)i0, kWave - 1);
+    f0 = wave_scan_f32(m0);
+    f1 = wave_scan_f32(m1) + readlane_f(f0, kWave - 1);
+    const unsigned long long h0 = __ballot(i0 >= k), h1 = __ballot(i1 >= k);
+    if (!h0 && !h1) return o;   // fewer than k entries in the window
+    ok_blk = h0 ? __ffsll((long long)h0) - 1 : kWave + __ffsll((long long)h1) - 1;
+    const uint32_t inc = ok_blk < kWave ? (uint32_t)__builtin_amdgcn_readlane((int)i0, ok_blk)
+                                        : (uint32_t)__builtin_amdgcn_readlane((int)i1, ok_blk - kWave);
+    const uint32_t own = ok_blk < kWave ? (uint32_t)__builtin_amdgcn_readlane((int)c0, ok_blk)
+                                        : (uint32_t)__builtin_amdgcn_readlane((int)c1, ok_blk - kWave);
+    cbase = inc - own;
+    const int32_t pb = ok_blk - 1;
+    mbase = pb < 0 ? 0.0f : pb < kWave ? readlane_f(f0, pb) : readlane_f(f1, pb - kWave);
+    // the ok_blk-th occupied block from the top
+    int32_t b = occupied_below(occ_lo, occ_hi, (hi >> 8) + 1);
+    for (int32_t t = 0; t < ok_blk; ++t) b = occupied_below(occ_lo, occ_hi, b);
+    top1 = b * 256 + 255;
+    in_first = top1 == hi;
+  }
   uint32_t cc[4];
   float mm[4], mx[4];   // per bin: count, mass, mass of the bins above it
-  for (int32_t top = hi; top >= lo; top -= 4 * kWave) {
-    if (so && !chunk_any(hist, top, lo, lane)) {   // an empty chunk: nothing to add up
+  for (int32_t top = top1; top >= lo; top -= 4 * kWave) {
+    if (so && !chunk_occupied(occ_lo, occ_hi, top, lo)) {   // an empty chunk: nothing to add up
       in_first = false;
+      top = skip_empty(occ_lo, occ_hi, top, lo);
       continue;
     }
     uint32_t cs = 0;
@@ -465,9 +570,26 @@ __device__ __forceinline__ ScanOut scan_hist(const uint32_t* hist, int32_t lo, i
     return o;
   }
   float mb = 0.0f;
-  for (int32_t top = hi; top >= o.tau_bits; top -= 4 * kWave) {
+  int32_t top2 = hi;
+  if (bidx) {
+    // the first block from the top whose cumulative mass reaches the target
+    // (with a margin for the order of the additions), at the latest the k-th
+    // value's block
+    const float tm = target * (1.0f - 0x1p-10f);
+    const unsigned long long g0 = __ballot(lane < ok_blk && f0 >= tm);
+    const unsigned long long g1 = __ballot(lane + kWave < ok_blk && f1 >= tm);
+    const int32_t pb = g0 ? __ffsll((long long)g0) - 1 : g1 ? kWave + __ffsll((long long)g1) - 1 : ok_blk;
+    mb = pb == 0 ? 0.0f : pb - 1 < kWave ? readlane_f(f0, pb - 1) : readlane_f(f1, pb - 1 - kWave);
+    int32_t b = occupied_below(occ_lo, occ_hi, (hi >> 8) + 1);
+    for (int32_t t = 0; t < pb; ++t) b = occupied_below(occ_lo, occ_hi, b);
+    top2 = b * 256 + 255;
+  }
+  for (int32_t top = top2; top >= o.tau_bits; top -= 4 * kWave) {
     // an empty chunk (the bin at tau is never empty): nothing to add up
-    if (so && !chunk_any(hist, top, o.tau_bits, lane)) continue;
+    if (so && !chunk_occupied(occ_lo, occ_hi, top, o.tau_bits)) {
+      top = skip_empty(occ_lo, occ_hi, top, o.tau_bits);
+      continue;
+    }
     bool ne[4];
     float ms = 0.0f;
 #pragma unroll
@@ -954,6 +1076,9 @@ __device__ __forceinline__ int topk_body(const RowArgs& a, int r, int64_t src, i
       fs.tmax = 0;
       fs.kmax = 0;
     }
+    if constexpr (sgn) {
+      if (tid < 4) fs.occ[tid] = 0;
+    }
   }
   __syncthreads();
 
@@ -1055,6 +1180,12 @@ __device__ __forceinline__ int topk_body(const RowArgs& a, int r, int64_t src, i
     wave_lds_sync();
     const int32_t tc = max(max(t16, (int32_t)fs.tmax - 0x8000), tlo);
     const i16x2 tc2 = __builtin_bit_cast(i16x2, (uint32_t)tc * 0x10001u);
+    // signed order: also mark the key's 256-key block, so that the scan passes
+    // over the empty stretches of the wide window without reading them
+    auto count_key = [&](int32_t key) {
+      hist_add(fs.hist, key);
+      if constexpr (sgn) atomicOr(&fs.occ[key >> 13], 1u << ((key >> 8) & 31));
+    };
     for (uint32_t e = lane; e < stored; e += kWave) {
       const int32_t vmx = (int32_t)my_vim[e] >> 16;
       if (vmx < tc) continue;
@@ -1066,12 +1197,12 @@ __device__ __forceinline__ int topk_body(const RowArgs& a, int r, int64_t src, i
         nlt += (uint32_t)__popc(__builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(
                                     __builtin_bit_cast(i16x2, word_of(dv, w)), tc2)) & 0x80008000u);
       if (nlt == 7) {                // the maximum is the only entry >= tc
-        hist_add(fs.hist, sgn ? zkey(vmx) + hoff : vmx);
+        count_key(sgn ? zkey(vmx) + hoff : vmx);
       } else {
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
           const int32_t val = elem_i16(dv, s);
-          if (val >= tc) hist_add(fs.hist, sgn ? zkey(val) + hoff : val);
+          if (val >= tc) count_key(sgn ? zkey(val) + hoff : val);
         }
       }
     }
@@ -1085,6 +1216,19 @@ __device__ __forceinline__ int topk_body(const RowArgs& a, int r, int64_t src, i
   __syncthreads();
 
   // ---- 3. wave 0 scans the histogram from the row maximum down to t* = max_w t_w
+  // (signed order: after every wave has added up some of the window's
+  // occupied blocks)
+  int32_t nblk = -1;
+  if constexpr (sgn) {
+    const int32_t kmax16 = (int32_t)fs.kmax - 0x8000;
+    const int32_t tstar16 = (int32_t)fs.tmax - 0x8000;
+    const int32_t lo = max(zkey(tstar16), -hoff) + hoff;
+    const int32_t hi = zkey(kmax16) + hoff;
+    if (fs.flag == 0 && kmax16 <= kPosInfBits && (hi & 255) == 255 && lo <= hi)
+      nblk = block_totals(fs.hist, fs.occ, fs.bcnt, fs.bmass, lo, hi, inv_t,
+                          __fmul_rn(pat_value(kmax16, true), inv_t), hoff, wid, lane);
+    __syncthreads();
+  }
   float m = 0.0f;                   // row maximum / T (wave 0)
   if (wid == 0) {
     // the row maximum and t* = max_w t_w, published with LDS atomics (a wave
@@ -1101,7 +1245,8 @@ __device__ __forceinline__ int topk_body(const RowArgs& a, int r, int64_t src, i
     if (usable) {
       const int32_t lo = sgn ? max(zkey(tstar16), -hoff) + hoff : tstar16;
       const int32_t hi = sgn ? zkey(kmax16) + hoff : kmax16;
-      so = scan_hist(fs.hist, lo, hi, inv_t, m, (uint32_t)kq, p_on, pq, hoff, sgn);
+      so = scan_hist(fs.hist, fs.occ, lo, hi, inv_t, m, (uint32_t)kq, p_on, pq, hoff, sgn, fs.bcnt,
+                     fs.bmass, nblk);
       if constexpr (sgn) {
         // keys back to patterns; a cut in the zone has no exact pattern
         if (so.tau_bits == hoff || so.vc_bits == hoff) so.ok = false;
