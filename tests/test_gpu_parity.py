@@ -334,6 +334,34 @@ def test_bf16_rows_cut_at_or_below_zero(k, p, t):
     _run_custom(wl)
 
 
+def _binade_rows(v, seed):
+    """bf16 rows whose 172 largest entries lie one per binary exponent, from
+    +2^60 (+2^20 in the last row) down through the signed zero region to
+    -2^-10 (-2^30), over a floor of -2^100 that stays outside every top-k
+    below: the signed-order pass's window holds 60 to 90 occupied 256-key
+    blocks above the k-th value (its scan's block index past 64 blocks)."""
+    rng = np.random.default_rng(seed)
+    rows = np.full((5, v), -2.0 ** 100, dtype=np.float32)
+    for r in range(5):
+        top_e, low_e = (60, -10) if r < 4 else (20, 30)
+        pos = np.ldexp(1.0 + rng.integers(0, 128, top_e + 61) / 128.0, np.arange(-60, top_e + 1))
+        neg = -np.ldexp(1.0 + rng.integers(0, 128, low_e + 61) / 128.0, np.arange(-60, low_e + 1))
+        vals = np.concatenate([pos, neg])
+        rows[r, rng.choice(v, vals.size, replace=False)] = vals
+    return rows
+
+
+@pytest.mark.parametrize("k,p,t", [(150, 1.0, 2.0 ** 57), (150, 0.99, 2.0 ** 57), (100, 0.9, 2.0 ** 56),
+                                   (172, 0.999, 2.0 ** 58)])
+def test_bf16_rows_top_k_spanning_many_binades(k, p, t):
+    """The signed-order pass on a window whose occupied blocks above the k-th
+    value (and above the top-p cutoff) number more than one wave's lanes."""
+    rows = _binade_rows(16384, 91 + k)
+    wl = _custom(rows, torch.bfloat16, k=k, p=p, t=t)
+    print(f"[case] binade bf16 k={k} p={p} t={t}", flush=True)
+    _run_custom(wl)
+
+
 def _small_f32_rows(v, seed):
     """fp32 rows for the short-row kernel: heavy ties, signed zeros, -inf and
     NaN sprinkled in, one row with fewer finite entries than most k, one flat
