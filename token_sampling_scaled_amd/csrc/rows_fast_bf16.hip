@@ -95,6 +95,11 @@ struct FastShared {
 // Rows without an active top-k: an exact histogram of order keys over the
 // window [kmax - 32767, kmax] below the row maximum (one bin per bf16 value).
 constexpr int kNoKBins = 32768;
+constexpr int kNoKDrainEvery = 2;   // vectors between draws of the top-p draw's queue
+// queued member groups per wave: fewer than 64 left over, plus 2 groups of
+// every lane of kNoKDrainEvery vectors
+constexpr int kNoKQueue = 64 + 2 * 64 * kNoKDrainEvery;
+static_assert(3 * kNoKQueue * (1024 / 64) <= kNoKBins, "the queues live in the histogram's LDS");
 struct NoKShared {
   uint32_t hist[kNoKBins];
   uint32_t wkey[kWv];
@@ -940,32 +945,89 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
   }
 
   // ---- Philox noise for the members of P (x at or above the cutoff group's
-  // value: -0 with +0, never -inf), perturbed argmax.  A lane whose block of
-  // four entries holds no member skips its Philox block.
+  // value: -0 with +0, never -inf), perturbed argmax.  Each wave queues its
+  // 4-entry groups holding a member, with their raw words, in LDS (the
+  // histogram's, free by now) from a ballot, and draws one Philox block per
+  // queued group, 64 at a time: every lane of a draw holds a member group,
+  // where drawing in place ran the block for every lane whenever one of them
+  // held a member.
   const float x_thr = key_value(vc_key);
   const NoiseStream nst{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)r,
                         (uint32_t)off, (uint32_t)(off >> 32)};
-  Pick best{-__builtin_inff(), 0x7FFFFFFF, 0.0f};
+  uint32_t* qg = ns_.hist + wid * (3 * kNoKQueue);   // queued group ids
+  uint32_t* qw = qg + kNoKQueue;                     // their two raw words each
+  float bz = -__builtin_inff(), bs = 0.0f;
+  int32_t bj = 0x7FFFFFFF;
+  uint32_t fill = 0;                                  // queued groups (wave-uniform)
+  auto drain_from = [&](uint32_t first, uint32_t count) {   // draw count (<= 64) queued groups
+    if ((uint32_t)lane < count) {
+      const uint32_t q = first + (uint32_t)lane;
+      const uint32_t g = qg[q];
+      const uint32_t ua = qw[2 * q], ub = qw[2 * q + 1];
+      const float x[4] = {__uint_as_float(ua << 16), __uint_as_float(ua & 0xFFFF0000u),
+                          __uint_as_float(ub << 16), __uint_as_float(ub & 0xFFFF0000u)};
+      const Philox4 wds = nst.block(g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (!(x[e] >= x_thr)) continue;
+        const float sv = __fmul_rn(x[e], inv_t);
+        const float zz = sv + gumbel_from_word(wds.v[e]);
+        const int32_t j = (int32_t)(g * 4u + (uint32_t)e);
+        if (better(zz, j, bz, bj)) {
+          bz = zz;
+          bj = j;
+          bs = sv;
+        }
+      }
+    }
+  };
+  // every kNoKDrainEvery vectors: draw the full rounds of 64 queued groups and
+  // move the rest to the front
+  auto drain_rounds = [&]() {
+    wave_lds_sync();
+    uint32_t first = 0;
+    for (; fill - first >= (uint32_t)kWave; first += kWave) drain_from(first, kWave);
+    const uint32_t rest = fill - first;
+    uint32_t mg = 0, ma = 0, mb2 = 0;
+    if ((uint32_t)lane < rest) {
+      mg = qg[first + lane];
+      ma = qw[2 * (first + lane)];
+      mb2 = qw[2 * (first + lane) + 1];
+    }
+    __builtin_amdgcn_wave_barrier();
+    if ((uint32_t)lane < rest) {
+      qg[lane] = mg;
+      qw[2 * lane] = ma;
+      qw[2 * lane + 1] = mb2;
+    }
+    fill = rest;
+  };
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int vi = i * kB + tid;
-    if (!(i < nfull || vi < nvec)) continue;
+    const bool valid = i < nfull || vi < nvec;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       // entries 4h .. 4h + 3 of the vector: one Philox block
       const uint32_t ua = word_of(d[i], 2 * h), ub = word_of(d[i], 2 * h + 1);
-      const float x[4] = {__uint_as_float(ua << 16), __uint_as_float(ua & 0xFFFF0000u),
-                          __uint_as_float(ub << 16), __uint_as_float(ub & 0xFFFF0000u)};
-      if (!(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])) >= x_thr)) continue;
-      const Philox4 wds = nst.block((uint32_t)(2 * vi + h));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float sv = __fmul_rn(x[e], inv_t);
-        const float zz = sv + gumbel_from_word(wds.v[e]);
-        if (x[e] >= x_thr && zz > best.z) best = Pick{zz, vi * 8 + 4 * h + e, sv};   // j rises within a thread
+      const float xm = fmaxf(fmaxf(__uint_as_float(ua << 16), __uint_as_float(ua & 0xFFFF0000u)),
+                             fmaxf(__uint_as_float(ub << 16), __uint_as_float(ub & 0xFFFF0000u)));
+      const bool mem = valid && xm >= x_thr;
+      const unsigned long long mm = __ballot(mem);
+      if (mem) {
+        const uint32_t pos = fill + lane_rank(mm);
+        qg[pos] = (uint32_t)(2 * vi + h);
+        qw[2 * pos] = ua;
+        qw[2 * pos + 1] = ub;
       }
+      fill += (uint32_t)__popcll(mm);
     }
+    if ((i + 1) % kNoKDrainEvery == 0 && i + 1 < NV) drain_rounds();
   }
+  wave_lds_sync();
+  for (uint32_t first = 0; first < fill; first += kWave)
+    drain_from(first, fill - first < (uint32_t)kWave ? fill - first : (uint32_t)kWave);
+  Pick best{bz, bj, bs};
   best = block_pick(best, sh.f);
   if (tid == 0) write_result(a, r, best.j, best.s - m - __logf(zp));
   return true;
