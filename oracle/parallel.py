@@ -23,8 +23,8 @@ import numpy as np
 
 from . import sampler
 
-# A GPU machine grants one GPU's share of its host cores; more workers than that
-# only compete for them.
+# A machine with one GPU per process typically gives a process about 16 host
+# cores; more workers than that only compete for them.
 MAX_WORKERS = 16
 
 
