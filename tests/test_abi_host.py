@@ -177,3 +177,19 @@ def test_verify_chain_argument_checks(lib):
         ptrs = [FAKE] * 5
         ptrs[k] = None
         assert lib.ts_verify_chain(2, 4, *ptrs, None) == tsa.TS_E_ARG
+
+
+def test_stage_marks_only_in_the_marks_build(lib):
+    # the product library compiles the stage marks out; the marks build
+    # (python -m token_sampling_scaled_amd.build --stage-marks) exports them
+    from token_sampling_scaled_amd import build
+    assert not hasattr(lib, "tss_stage_marks")
+    if not os.path.exists(build.MARKS_LIB):
+        pytest.skip("libtssample_marks.so not built")
+    marks = ctypes.CDLL(build.MARKS_LIB)
+    assert hasattr(marks, "tss_stage_marks") and hasattr(marks, "tss_stage_marks_clear")
+    marks.tss_stage_marks.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    # argument errors return 0 before any HIP call
+    assert marks.tss_stage_marks(None, 4) == 0
+    assert marks.tss_stage_marks(ctypes.c_void_p(FAKE), 0) == 0
+    assert marks.tss_stage_marks(ctypes.c_void_p(FAKE), 1025) == 0

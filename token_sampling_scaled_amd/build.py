@@ -1,6 +1,9 @@
 """Build libtssample.so and libtsprobe.so (gfx950) in-tree with hipcc.
 
     python -m token_sampling_scaled_amd.build          # compile every source
+    python -m token_sampling_scaled_amd.build --stage-marks
+        # also libtssample_marks.so: the sampler with stage marks in the
+        # register-resident kernel (token_sampling_scaled_amd.stage_times)
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
 generation switched off.  csrc/ (kernels and the C-ABI host code) links into
@@ -22,6 +25,7 @@ INCLUDE = os.path.join(ROOT, "include")
 PROBE = os.path.join(PKG, "csrc_probe")
 LIB = os.path.join(PKG, "libtssample.so")
 PROBE_LIB = os.path.join(PKG, "libtsprobe.so")
+MARKS_LIB = os.path.join(PKG, "libtssample_marks.so")
 
 ARCH = "gfx950"
 HIP_FLAGS = [
@@ -49,7 +53,13 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB
 
 
-def _build_lib(srcs, lib_path: str, verbose: bool, jobs: int) -> None:
+def build_stage_marks(verbose: bool = False, jobs: int = 8) -> str:
+    """The sampler with stage marks compiled in, beside the product library."""
+    _build_lib(sources(CSRC), MARKS_LIB, verbose, jobs, defines=["-DTSS_STAGE_MARKS"])
+    return MARKS_LIB
+
+
+def _build_lib(srcs, lib_path: str, verbose: bool, jobs: int, defines=()) -> None:
     cc = hipcc()
     objdir = tempfile.mkdtemp(prefix="tssample_build_")
     try:
@@ -58,7 +68,7 @@ def _build_lib(srcs, lib_path: str, verbose: bool, jobs: int) -> None:
         for src in srcs:
             obj = os.path.join(objdir, os.path.basename(src) + ".o")
             objs.append(obj)
-            cmd = [cc, *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", src, "-o", obj]
+            cmd = [cc, *HIP_FLAGS, *defines, f"-I{INCLUDE}", f"-I{CSRC}", "-c", src, "-o", obj]
             if src.endswith(".cpp"):
                 cmd[1:1] = ["-x", "hip"]
             if verbose:
@@ -90,3 +100,5 @@ def _wait(item):
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    if "--stage-marks" in sys.argv:
+        print(build_stage_marks(verbose="-v" in sys.argv))

@@ -40,6 +40,48 @@
 // same workgroup.
 #include "general_row.hpp"
 
+// Stage marks (a build with TSS_STAGE_MARKS defined only, a separate library):
+// thread 0 of workgroup b < kStageRows (output row b, unless rows outnumber the
+// compute units and heavy rows go first) records the device's constant-rate
+// wall clock at each stage of the top-k body; the default build compiles the
+// marks to nothing.
+#ifdef TSS_STAGE_MARKS
+namespace tss {
+constexpr int kStageRows = 1024;
+constexpr int kStageMarks = 8;
+__device__ unsigned long long g_stage_marks[kStageRows * kStageMarks];
+}  // namespace tss
+#define TSS_MARK(k)                                                                       \
+  do {                                                                                    \
+    if (threadIdx.x == 0 && blockIdx.x < (unsigned)::tss::kStageRows)                    \
+      ::tss::g_stage_marks[blockIdx.x * ::tss::kStageMarks + (k)] = wall_clock64();       \
+  } while (0)
+// Copies the marks of workgroups [0, rows) to host memory ([rows][8] uint64:
+// 0 start, 1 threshold, 2 data offered, 3 counted, 4 scanned, 5 listed,
+// 6 picked, 7 signed-order pass started; 0 for a stage not reached since the
+// last clear, else the last call's) and returns the wall clock's rate in kHz
+// (0 on an error).
+extern "C" int tss_stage_marks(unsigned long long* host, int rows) {
+  if (host == nullptr || rows < 1 || rows > ::tss::kStageRows) return 0;
+  if (hipDeviceSynchronize() != hipSuccess) return 0;
+  if (hipMemcpyFromSymbol(host, HIP_SYMBOL(::tss::g_stage_marks),
+                          sizeof(unsigned long long) * ::tss::kStageMarks * rows) != hipSuccess)
+    return 0;
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, 0) != hipSuccess) return 0;
+  return khz;
+}
+// Clears the marks (between workloads).
+extern "C" int tss_stage_marks_clear() {
+  static const unsigned long long zeros[1024 * 8] = {};
+  return hipMemcpyToSymbol(HIP_SYMBOL(::tss::g_stage_marks), zeros, sizeof(zeros)) == hipSuccess;
+}
+#else
+#define TSS_MARK(k) \
+  do {              \
+  } while (0)
+#endif
+
 namespace tss {
 
 namespace {
@@ -1190,6 +1232,7 @@ __device__ __forceinline__ int topk_body(const RowArgs& a, int r, int64_t src, i
 
   // ---- 2. filter vectors into this wave's segment as they arrive, then count
   // their entries
+  TSS_MARK(1);                      // threshold
   uint32_t wfill = 0;               // wave-uniform number of vectors offered
   v4u* my_vec = fs.cvec[wid];
   uint32_t* my_vim = fs.cvim[wid];
@@ -1224,6 +1267,7 @@ __device__ __forceinline__ int topk_body(const RowArgs& a, int r, int64_t src, i
       offer(i, mv);
     }
   }
+  TSS_MARK(2);                      // the wave's data all in and offered
   if (lane == 0 && wfill > (uint32_t)kSegV) fs.flag = 1;   // a full segment lost vectors
   const uint32_t stored = wfill < (uint32_t)kSegV ? wfill : (uint32_t)kSegV;
   // signed order: the row maximum places the histogram's window before any
@@ -1276,6 +1320,7 @@ __device__ __forceinline__ int topk_body(const RowArgs& a, int r, int64_t src, i
     atomicMax(&fs.kmax, wmaxu);
   }
   __syncthreads();
+  TSS_MARK(3);                      // counted, first barrier
 
   // ---- 3. wave 0 scans the histogram from the row maximum down to t* = max_w t_w
   // (signed order: after every wave has added up some of the window's
@@ -1327,6 +1372,7 @@ __device__ __forceinline__ int topk_body(const RowArgs& a, int r, int64_t src, i
     }
   }
   __syncthreads();
+  TSS_MARK(4);                      // scanned, second barrier
   const uint32_t scan_ok = fs.scan_ok;
   if (scan_ok != 1u)
     return (kSignedPass<NV, ROUTE, MODE> && !sgn && scan_ok == 2u) ? kBodyRetry : kBodyGeneral;
@@ -1456,6 +1502,7 @@ __device__ __forceinline__ int topk_body(const RowArgs& a, int r, int64_t src, i
     }
   }
   __syncthreads();
+  TSS_MARK(5);                      // listed, third barrier
   const uint32_t nmv = fs.np;
   const uint32_t nt = tie_cut ? fs.nties : 0u;
   if (nmv > (uint32_t)kMaxK || nt > (uint32_t)kMaxTies) {
@@ -1501,10 +1548,12 @@ __device__ __forceinline__ int topk_body(const RowArgs& a, int r, int64_t src, i
   if (one_wave) {
     best = wave_pick(best);
     if (lane == 0) write_result(a, r, best.j, best.s - m - __logf(fs.zp));
+    TSS_MARK(6);                    // drawn and picked
     return kBodyDone;
   }
   best = block_pick(best, fs);
   if (tid == 0) write_result(a, r, best.j, best.s - m - __logf(fs.zp));
+  TSS_MARK(6);                      // drawn and picked
   return kBodyDone;
 }
 
@@ -1519,6 +1568,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
   __shared__ uint64_t cls[kWv];
   FastShared& fs = sh.f;
 
+  TSS_MARK(0);                      // start
   const int r = a.heavy_first ? heavy_first_row<ROUTE, MODE>(a, cls) : (int)blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t src = a.gather ? (int64_t)a.gather[r] : (int64_t)r;
@@ -1575,6 +1625,7 @@ __global__ __launch_bounds__(kB) void rows_fast_bf16_kernel(RowArgs a) {
                                            inv_t, sh);
     if (kSignedPass<NV, ROUTE, MODE> && st == kBodyRetry) {
       // a wave threshold <= +0: the steps again, in signed order, on the row read again
+      TSS_MARK(7);
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int vi = i * kB + tid;
