@@ -48,7 +48,7 @@
 #ifdef TSS_STAGE_MARKS
 namespace tss {
 constexpr int kStageRows = 1024;
-constexpr int kStageMarks = 8;
+constexpr int kStageMarks = 16;
 __device__ unsigned long long g_stage_marks[kStageRows * kStageMarks];
 }  // namespace tss
 #define TSS_MARK(k)                                                                       \
@@ -56,11 +56,13 @@ __device__ unsigned long long g_stage_marks[kStageRows * kStageMarks];
     if (threadIdx.x == 0 && blockIdx.x < (unsigned)::tss::kStageRows)                    \
       ::tss::g_stage_marks[blockIdx.x * ::tss::kStageMarks + (k)] = wall_clock64();       \
   } while (0)
-// Copies the marks of workgroups [0, rows) to host memory ([rows][8] uint64:
-// 0 start, 1 threshold, 2 data offered, 3 counted, 4 scanned, 5 listed,
-// 6 picked, 7 signed-order pass started; 0 for a stage not reached since the
-// last clear, else the last call's) and returns the wall clock's rate in kHz
-// (0 on an error).
+// Copies the marks of workgroups [0, rows) to host memory ([rows][16] uint64:
+// 0 start; top-k body: 1 threshold, 2 data offered, 3 counted, 4 scanned,
+// 5 listed, 6 picked, 7 signed-order pass started; rows without top-k (sampling):
+// 8 row maximum, 9 Z, 10 histogram counted, 11 cutoff found, 12 drawn (the
+// race, for rows without top-p), 13 picked; 0 for a stage not reached since
+// the last clear, else the last call's) and returns the wall clock's rate in
+// kHz (0 on an error).
 extern "C" int tss_stage_marks(unsigned long long* host, int rows) {
   if (host == nullptr || rows < 1 || rows > ::tss::kStageRows) return 0;
   if (hipDeviceSynchronize() != hipSuccess) return 0;
@@ -73,7 +75,7 @@ extern "C" int tss_stage_marks(unsigned long long* host, int rows) {
 }
 // Clears the marks (between workloads).
 extern "C" int tss_stage_marks_clear() {
-  static const unsigned long long zeros[1024 * 8] = {};
+  static const unsigned long long zeros[1024 * 16] = {};
   return hipMemcpyToSymbol(HIP_SYMBOL(::tss::g_stage_marks), zeros, sizeof(zeros)) == hipSuccess;
 }
 #else
@@ -748,6 +750,7 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
   }
   __syncthreads();
   kmx = wave_max_dpp(lane < kWv ? ns_.wkey[lane] : 0u);
+  TSS_MARK(8);
   const uint32_t any_nan_lo = wave_max_dpp(lane < kWv ? ns_.wnan[lane] : 0u);
   if (kmx >= kPosInfKey || any_nan_lo != 0) return false;   // NaN or +inf: general body
   if (kmx <= kNegInfKey) {                        // no finite entry: id -1 and lp NaN
@@ -815,6 +818,7 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
     // its maximum, so some thread's wb is positive; a thread with none keeps -inf)
     Pick p{wb > 0.0f ? __builtin_amdgcn_logf(wb) - __builtin_amdgcn_logf(eb) : -__builtin_inff(), jb,
            __fmul_rn(xb, inv_t)};
+    TSS_MARK(12);
     z = wave_sum(z);
     p = wave_pick(p);
     if (lane == 0) {
@@ -832,6 +836,7 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
       if (lane < kWv) b = Pick{ns_.wpz[lane], ns_.wpj[lane], ns_.wps[lane]};
       b = wave_pick(b);
       if (lane == 0) write_result(a, r, b.j, b.s - m - __logf(zt));
+      TSS_MARK(13);
     }
     return true;
   }
@@ -851,6 +856,7 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
   z = wave_sum(z);
   if (lane == 0) ns_.wz[wid] = z;
   __syncthreads();
+  TSS_MARK(9);
   z = 0.0f;
 #pragma unroll
   for (int w = 0; w < kWv; ++w) z += ns_.wz[w];
@@ -888,6 +894,7 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
       }
     }
     __syncthreads();
+    TSS_MARK(10);
     // ---- wave 0 scans the bins from the maximum down: the cutoff group is
     // the first nonempty one whose cumulative mass reaches p Z (the top group
     // is always kept)
@@ -940,6 +947,7 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
     }
     __syncthreads();
     if (ns_.ok == 0) return false;
+    TSS_MARK(11);
     vc_key = ns_.vc_key;
     zp = ns_.zp;
   }
@@ -1069,9 +1077,11 @@ __device__ __forceinline__ bool nok_row(const RowArgs& a, int r, int nvec, int n
   wave_lds_sync();
   for (uint32_t first = 0; first < fill; first += kWave)
     drain_from(first, fill - first < (uint32_t)kWave ? fill - first : (uint32_t)kWave);
+  TSS_MARK(12);
   Pick best{bz, bj, bs};
   best = block_pick(best, sh.f);
   if (tid == 0) write_result(a, r, best.j, best.s - m - __logf(zp));
+  TSS_MARK(13);
   return true;
 }
 

@@ -5,9 +5,10 @@
 
 Loads libtssample_marks.so (the sampler built with TSS_STAGE_MARKS: thread 0
 of each workgroup records the device's wall clock at each stage of the top-k
-body), samples the workload a few times, and prints over the workgroups of the
-last call the median of each stage, the spread of the starts, the median and
-the last end, and the slowest workgroups' stages.  Times are in microseconds
+body and of the sampling body of rows without top-k), samples the workload a
+few times, and prints over the workgroups of the last call the median of each
+stage, the spread of the starts, the median and the last end, and the slowest
+workgroups' stages.  Times are in microseconds
 from the first workgroup's start.  The library must exist: nothing here
 builds it or falls back to another.
 """
@@ -23,6 +24,9 @@ import numpy as np
 
 STAGES = ["threshold", "data offered", "counted + barrier", "scanned + barrier",
           "listed + barrier", "drawn + picked"]
+NOK_STAGES = ["row maximum + barrier", "Z + barrier", "histogram + barrier", "cutoff + barrier",
+              "draw", "pick"]
+NMARKS = 16
 
 
 def _setup(workload: str):
@@ -67,12 +71,12 @@ def stage_table(workload: str, calls: int = 5, slowest: int = 6) -> dict:
     for _ in range(calls):
         call()
     torch.cuda.synchronize()
-    buf = np.zeros((rows, 8), dtype=np.uint64)
+    buf = np.zeros((rows, NMARKS), dtype=np.uint64)
     khz = marks.tss_stage_marks(buf.ctypes.data, rows)
     if khz <= 0:
         raise RuntimeError("tss_stage_marks failed")
     t = buf.astype(np.float64) / (khz / 1000.0)          # microseconds
-    seen = buf[:, 6] > 0                                 # workgroups that finished the body
+    seen = buf[:, 6] > 0                                 # workgroups that finished the top-k body
     t0 = t[buf[:, 0] > 0, 0].min()
     out = {"workload": workload, "workgroups": int(rows), "through_top_k_body": int(seen.sum()),
            "signed_pass": int((buf[:, 7] > 0).sum())}
@@ -95,6 +99,25 @@ def stage_table(workload: str, calls: int = 5, slowest: int = 6) -> dict:
         out["slowest"] = [{"workgroup": int(b), "end_us": round(float(t[b, 6] - t0), 2),
                            "stages_us": [round(float(st[b, i + 1] - st[b, i]), 2) for i in range(6)]}
                           for b in order if seen[b]]
+    # rows without top-k (sampling): top-p rows pass marks 8 to 13, the race
+    # rows (no top-p) 8, 12 and 13
+    nok = buf[:, 13] > 0
+    topp = nok & (buf[:, 11] > 0)
+    race = nok & ~topp
+    if topp.any():
+        marks = [0, 8, 9, 10, 11, 12, 13]
+        out["top_p_rows"] = int(topp.sum())
+        out["top_p_stage_median_us"] = {
+            name: round(float(np.median(t[topp, marks[i + 1]] - t[topp, marks[i]])), 2)
+            for i, name in enumerate(NOK_STAGES)}
+        out["top_p_end_max_us"] = round(float((t[topp, 13] - t0).max()), 2)
+    if race.any():
+        out["race_rows"] = int(race.sum())
+        out["race_stage_median_us"] = {
+            "row maximum + barrier": round(float(np.median(t[race, 8] - t[race, 0])), 2),
+            "Z and the race": round(float(np.median(t[race, 12] - t[race, 8])), 2),
+            "pick": round(float(np.median(t[race, 13] - t[race, 12])), 2)}
+        out["race_end_max_us"] = round(float((t[race, 13] - t0).max()), 2)
     return out
 
 
