@@ -32,8 +32,11 @@
 // values that is the value order and every negative value sorts below them, so
 // it is exact whenever every t_w > +0.  A row with some t_w <= +0 runs steps
 // 1-5 again on the row read again and taken to two's-complement order, with
-// the patterns of |x| < 2^-64 sharing one histogram key (see sord2 and zkey).
-// Rows without top-k run nok_row (the whole row in registers).  Greedy rows
+// the patterns of |x| < 2^-64 sharing one histogram key (see sord2 and zkey);
+// its wider, mostly empty window is scanned from per-block totals that every
+// wave adds up (block_totals).  Rows without top-k run nok_row (the whole row
+// in registers; top-p rows draw from a per-wave queue of member groups).
+// Greedy rows
 // take the first maximum.  Every other row -- k > 1024, NaN logits, a full LDS
 // segment, fewer than k counted entries at or above t*, a cut inside the
 // collapsed zone -- runs the general per-row body (general_row.hpp) on the
